@@ -1,0 +1,214 @@
+// mq_api.hip -- the C ABI declared in include/mq.h: host-side validation,
+// kernel choice, launches.  No memory is allocated and no state is kept.
+#include <stdint.h>
+
+#include "../../include/mq.h"
+#include "mq_kernels.h"
+
+namespace {
+
+using namespace mq;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_width(int r) { return r == 2 || r == 3 || r == 4 || r == 6 || r == 8; }
+
+mq_status check_shape(int n, int k) {
+  if (n <= 0 || k <= 0) return MQ_EINVAL;
+  if (k % 64) return MQ_ESHAPE;
+  return MQ_OK;
+}
+
+mq_status check_group(int k, int group) {
+  if (group <= 0) return MQ_ESHAPE;
+  if (group % 64 || k % group) return MQ_ESHAPE;
+  return MQ_OK;
+}
+
+// validate the packed parent for a width-r call and collect its plane pointers
+mq_status check_packed(const mq_packed* w, int r, int rule, PlanePtrs* out) {
+  if (!w) return MQ_EINVAL;
+  mq_status st = check_shape(w->n, w->k);
+  if (st != MQ_OK) return st;
+  if (rule != MQ_PREFIX && rule != MQ_ROUND) return MQ_ERULE;
+  if (!valid_width(r)) return MQ_EWIDTH;
+  const int np = planes_needed(r, rule == MQ_ROUND);
+  for (int p = 0; p < MQ_NPLANES; ++p) {
+    out->p[p] = static_cast<const uint32_t*>(w->plane[p]);
+    if (p < np) {
+      if (!w->plane[p]) return MQ_ENOPLANE;
+      if (!aligned16(w->plane[p])) return MQ_EALIGN;
+    }
+  }
+  return MQ_OK;
+}
+
+mq_status check_scales(const mq_packed* w, int group, const uint16_t* scales, const uint16_t* zeros) {
+  mq_status st = check_group(w->k, group);
+  if (st != MQ_OK) return st;
+  if (!scales || !zeros) return MQ_EINVAL;
+  if (!aligned16(scales) || !aligned16(zeros)) return MQ_EALIGN;
+  return MQ_OK;
+}
+
+mq_status validate_linear(const void* x, int x_dtype, int m, const mq_packed* w, int r, int rule, int group,
+                          const uint16_t* scales, const uint16_t* zeros, void* y, PlanePtrs* pl) {
+  if (m < 0) return MQ_EINVAL;
+  mq_status st = check_packed(w, r, rule, pl);
+  if (st != MQ_OK) return st;
+  st = check_scales(w, group, scales, zeros);
+  if (st != MQ_OK) return st;
+  if (x_dtype != MQ_F16 && x_dtype != MQ_BF16) return MQ_EDTYPE;
+  if (m == 0) return MQ_OK;
+  if (!x || !y) return MQ_EINVAL;
+  if (!aligned16(x) || !aligned16(y)) return MQ_EALIGN;
+  // kernels index with 64-bit offsets; keep grid dimensions in range
+  if ((long long)m * (long long)w->n > (1LL << 46) || (long long)w->n * (long long)w->k > (1LL << 46))
+    return MQ_ESIZE;
+  return MQ_OK;
+}
+
+mq_status run_linear(const void* x, int x_dtype, int m, const mq_packed* w, int r, int rule, int group,
+                     const uint16_t* scales, const uint16_t* zeros, void* y, void* workspace,
+                     size_t workspace_bytes, const PlanePtrs& pl, hipStream_t s) {
+  if (m == 0) return MQ_OK;
+  LinearArgs a;
+  a.x = x;
+  a.y = y;
+  a.pl = pl;
+  a.scales = scales;
+  a.zeros = zeros;
+  a.m = m;
+  a.n = w->n;
+  a.k = w->k;
+  a.group = group;
+  a.r = r;
+  a.round_rule = rule == MQ_ROUND;
+  a.bf16 = x_dtype == MQ_BF16;
+  hipError_t e;
+  if (gemv_eligible(m, w->k, a.bf16)) {
+    e = launch_gemv(a, s);
+  } else {
+    GemmPlan plan = plan_gemm(m, w->n, w->k, workspace ? workspace_bytes : 0);
+    if (plan.splits > 1 && !aligned16(workspace)) plan.splits = 1;
+    e = launch_gemm(a, plan, workspace, s);
+  }
+  return e == hipSuccess ? MQ_OK : MQ_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mq_status_str(mq_status s) {
+  switch (s) {
+    case MQ_OK: return "MQ_OK";
+    case MQ_EINVAL: return "MQ_EINVAL: null pointer or invalid size";
+    case MQ_EWIDTH: return "MQ_EWIDTH: width must be 2, 3, 4, 6 or 8";
+    case MQ_ESHAPE: return "MQ_ESHAPE: k % 64, group % 64, k % group or packed shape mismatch";
+    case MQ_EALIGN: return "MQ_EALIGN: device pointer not 16-byte aligned";
+    case MQ_ENOPLANE: return "MQ_ENOPLANE: a plane needed by (width, rule) is NULL";
+    case MQ_EDTYPE: return "MQ_EDTYPE: unsupported dtype";
+    case MQ_EHIP: return "MQ_EHIP: kernel launch failed";
+    case MQ_ERULE: return "MQ_ERULE: rule must be MQ_PREFIX or MQ_ROUND";
+    case MQ_ESIZE: return "MQ_ESIZE: size out of range";
+  }
+  return "MQ_UNKNOWN";
+}
+
+size_t mq_plane_bytes(int32_t n, int32_t k, int32_t plane) {
+  if (plane < 0 || plane >= MQ_NPLANES || check_shape(n, k) != MQ_OK) return 0;
+  return (size_t)n * (size_t)k * (size_t)kPlaneBits[plane] / 8;
+}
+
+int32_t mq_planes_needed(int32_t r, int32_t rule) {
+  if (!valid_width(r) || (rule != MQ_PREFIX && rule != MQ_ROUND)) return -1;
+  return planes_needed(r, rule == MQ_ROUND);
+}
+
+mq_status mq_pack_parent(const uint8_t* codes, int32_t n, int32_t k, const mq_packed* out, void* stream) {
+  if (!codes || !out) return MQ_EINVAL;
+  mq_status st = check_shape(n, k);
+  if (st != MQ_OK) return st;
+  if (out->n != n || out->k != k) return MQ_ESHAPE;
+  if (!aligned16(codes)) return MQ_EALIGN;
+  uint32_t* planes[MQ_NPLANES];
+  for (int p = 0; p < MQ_NPLANES; ++p) {
+    if (!out->plane[p]) return MQ_ENOPLANE;
+    if (!aligned16(out->plane[p])) return MQ_EALIGN;
+    planes[p] = static_cast<uint32_t*>(out->plane[p]);
+  }
+  return launch_pack(codes, n, k, planes, static_cast<hipStream_t>(stream)) == hipSuccess ? MQ_OK : MQ_EHIP;
+}
+
+size_t mq_linear_workspace_bytes(int32_t m, int32_t n, int32_t k) {
+  if (check_shape(n, k) != MQ_OK || m <= 0) return 0;
+  if (m <= kGemvMaxM && k <= kGemvMaxK && m == 1) return 0;
+  return gemm_workspace_bytes(m, n, k);
+}
+
+mq_status mq_linear(const void* x, int32_t x_dtype, int32_t m, const mq_packed* w, int32_t r, int32_t rule,
+                    int32_t group, const uint16_t* scales, const uint16_t* zeros, void* y, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  PlanePtrs pl;
+  mq_status st = validate_linear(x, x_dtype, m, w, r, rule, group, scales, zeros, y, &pl);
+  if (st != MQ_OK) return st;
+  return run_linear(x, x_dtype, m, w, r, rule, group, scales, zeros, y, workspace, workspace_bytes, pl,
+                    static_cast<hipStream_t>(stream));
+}
+
+mq_status mq_linear_mixed(const mq_call* calls, int32_t n_calls, void* workspace, size_t workspace_bytes,
+                          int32_t* failed_call, void* stream) {
+  if (failed_call) *failed_call = -1;
+  if (n_calls < 0 || (n_calls > 0 && !calls)) return MQ_EINVAL;
+  for (int32_t i = 0; i < n_calls; ++i) {
+    const mq_call& c = calls[i];
+    PlanePtrs pl;
+    mq_status st = validate_linear(c.x, c.x_dtype, c.m, c.w, c.r, c.rule, c.group, c.scales, c.zeros, c.y, &pl);
+    if (st != MQ_OK) {
+      if (failed_call) *failed_call = i;
+      return st;
+    }
+  }
+  for (int32_t i = 0; i < n_calls; ++i) {
+    const mq_call& c = calls[i];
+    PlanePtrs pl;
+    validate_linear(c.x, c.x_dtype, c.m, c.w, c.r, c.rule, c.group, c.scales, c.zeros, c.y, &pl);
+    mq_status st = run_linear(c.x, c.x_dtype, c.m, c.w, c.r, c.rule, c.group, c.scales, c.zeros, c.y, workspace,
+                              workspace_bytes, pl, static_cast<hipStream_t>(stream));
+    if (st != MQ_OK) {
+      if (failed_call) *failed_call = i;
+      return st;
+    }
+  }
+  return MQ_OK;
+}
+
+mq_status mq_slice_codes(const mq_packed* w, int32_t r, int32_t rule, uint8_t* codes_out, void* stream) {
+  PlanePtrs pl;
+  mq_status st = check_packed(w, r, rule, &pl);
+  if (st != MQ_OK) return st;
+  if (!codes_out) return MQ_EINVAL;
+  if (!aligned16(codes_out)) return MQ_EALIGN;
+  return launch_slice(pl, w->n, w->k, r, rule == MQ_ROUND, codes_out, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? MQ_OK
+             : MQ_EHIP;
+}
+
+mq_status mq_dequant(const mq_packed* w, int32_t r, int32_t rule, int32_t group, const uint16_t* scales,
+                     const uint16_t* zeros, int32_t out_dtype, void* w_out, void* stream) {
+  PlanePtrs pl;
+  mq_status st = check_packed(w, r, rule, &pl);
+  if (st != MQ_OK) return st;
+  st = check_scales(w, group, scales, zeros);
+  if (st != MQ_OK) return st;
+  if (out_dtype != MQ_F32 && out_dtype != MQ_F16 && out_dtype != MQ_BF16) return MQ_EDTYPE;
+  if (!w_out) return MQ_EINVAL;
+  if (!aligned16(w_out)) return MQ_EALIGN;
+  return launch_dequant(pl, w->n, w->k, r, rule == MQ_ROUND, group, scales, zeros, out_dtype, w_out,
+                        static_cast<hipStream_t>(stream)) == hipSuccess
+             ? MQ_OK
+             : MQ_EHIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,153 @@
+// mq_common.h -- device-side layout and slicing helpers shared by every libmq
+// kernel (packer, slice/dequant exports, GEMV, MFMA GEMM).
+//
+// Bit planes (MatGPTQ "Efficient and Accurate Inference over Nested Quantized
+// Models", section 4: buffers for bits 1-2, 3, 4, 5-6, 7-8 from the MSB):
+//   plane 0: bits 7..6   plane 1: bit 5   plane 2: bit 4
+//   plane 3: bits 3..2   plane 4: bits 1..0
+// Each plane is [n][k/32] units of 32 consecutive codes of one row.  A unit is
+// two 32-bit words for a 2-bit plane and one word for a 1-bit plane.
+//
+// Within a unit, code t (0..31) of a 2-bit plane lives in word t/16 at bit
+//   8*(t%4) + 2*((t%16)/4)
+// and code t of a 1-bit plane lives at bit
+//   8*(t%4) + t/4.
+// So for output word j (codes 4j..4j+3) one shift of the plane word by a
+// constant and one mask put the four codes' fields straight into their
+// natural place inside four bytes: after OR-ing the planes a unit becomes the
+// 32 truncated codes as bytes in k order.  No field ever crosses a byte.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mq {
+
+constexpr int kPlanes = 5;
+constexpr int kPlaneBits[kPlanes] = {2, 1, 1, 2, 2};
+// code bit index of each plane's lowest bit
+constexpr int kPlaneLsb[kPlanes] = {6, 5, 4, 2, 0};
+// offset of each plane's words in a packed "unit record" of 8 words
+constexpr int kUnitOff[kPlanes] = {0, 2, 3, 4, 6};
+constexpr int kUnitWords = 8;
+
+__host__ __device__ constexpr int planes_for_bits(int bits) {
+  return bits <= 2 ? 1 : bits == 3 ? 2 : bits == 4 ? 3 : bits <= 6 ? 4 : 5;
+}
+// leading bits covered by the first P planes
+__host__ __device__ constexpr int bits_of_planes(int P) {
+  return P <= 0 ? 0 : P == 1 ? 2 : P == 2 ? 3 : P == 3 ? 4 : P == 4 ? 6 : 8;
+}
+// planes read by a width-r call: PREFIX reads r bits, ROUND reads r+1 (r < 8)
+__host__ __device__ constexpr int planes_needed(int r, int round_rule) {
+  return planes_for_bits((round_rule && r < 8) ? r + 1 : r);
+}
+__host__ __device__ constexpr uint32_t rep4(uint32_t b) { return b * 0x01010101u; }
+
+template <int SH>
+__device__ __forceinline__ uint32_t shift_signed(uint32_t v) {
+  if constexpr (SH >= 0) return v << SH; else return v >> (-SH);
+}
+
+// Plane p's contribution to output word j (0..7) of a unit: the fields of
+// codes 4j..4j+3 moved to their code-bit position inside each byte.
+template <int P, int J>
+__device__ __forceinline__ uint32_t plane_part(const uint32_t* unit) {
+  if constexpr (kPlaneBits[P] == 2) {
+    constexpr int q = J % 4;
+    constexpr int sh = kPlaneLsb[P] - 2 * q;
+    return shift_signed<sh>(unit[kUnitOff[P] + J / 4]) & rep4(3u << kPlaneLsb[P]);
+  } else {
+    constexpr int sh = kPlaneLsb[P] - J;
+    return shift_signed<sh>(unit[kUnitOff[P]]) & rep4(1u << kPlaneLsb[P]);
+  }
+}
+
+template <int NP, int J, int P = 0>
+__device__ __forceinline__ uint32_t assemble_word_impl(const uint32_t* unit) {
+  if constexpr (P >= NP) {
+    return 0u;
+  } else {
+    return plane_part<P, J>(unit) | assemble_word_impl<NP, J, P + 1>(unit);
+  }
+}
+
+// Output word J of a unit from its first NP planes: four codes as bytes with
+// the planes' bits in place and all lower bits zero.
+template <int NP, int J>
+__device__ __forceinline__ uint32_t assemble_word(const uint32_t* unit) {
+  return assemble_word_impl<NP, J>(unit);
+}
+
+// Byte-domain value of the r-bit slice for four codes packed in one word,
+// before any centring offset:
+//   PREFIX: v = (q >> (8-r)) << (8-r)                       (<= 255, exact in a byte)
+//   ROUND : v = min(round_half_up(q / 2^(8-r)), 2^r - 1) << (8-r)
+// ROUND can overflow a byte before the clamp, so it is evaluated in 16-bit
+// lanes: `lo`/`hi` receive codes {0,1} and {2,3} as u16 pairs.
+template <int R, int ROUND>
+__device__ __forceinline__ void slice_pairs(uint32_t bytes, uint32_t& lo, uint32_t& hi) {
+  // v_perm_b32 selector: byte 0x0c yields 0x00
+  lo = __builtin_amdgcn_perm(0u, bytes, 0x0c010c00u);
+  hi = __builtin_amdgcn_perm(0u, bytes, 0x0c030c02u);
+  if constexpr (ROUND && R < 8) {
+    constexpr uint32_t keep = (0xFFu << (7 - R)) & 0xFFu;  // top r+1 bits
+    constexpr uint32_t half = 1u << (7 - R);               // the (r+1)-th bit
+    constexpr uint32_t lim = 256u - (1u << (8 - R));       // (2^r - 1) << (8-r)
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    u16x2 a = __builtin_bit_cast(u16x2, lo & (keep * 0x10001u));
+    u16x2 b = __builtin_bit_cast(u16x2, hi & (keep * 0x10001u));
+    const u16x2 hv = {(unsigned short)half, (unsigned short)half};
+    const u16x2 lv = {(unsigned short)lim, (unsigned short)lim};
+    a = a + (a & hv);
+    b = b + (b & hv);
+    a = __builtin_elementwise_min(a, lv);
+    b = __builtin_elementwise_min(b, lv);
+    lo = __builtin_bit_cast(uint32_t, a);
+    hi = __builtin_bit_cast(uint32_t, b);
+  }
+}
+
+// Same slice, kept as four bytes (valid after the clamp: v <= 255).
+template <int R, int ROUND>
+__device__ __forceinline__ uint32_t slice_bytes(uint32_t bytes) {
+  if constexpr (ROUND && R < 8) {
+    uint32_t lo, hi;
+    slice_pairs<R, ROUND>(bytes, lo, hi);
+    return __builtin_amdgcn_perm(hi, lo, 0x06040200u);
+  } else {
+    return bytes;
+  }
+}
+
+// centring offset delta_r = (2^(8-r) - 1) / 2 of the true-prefix rule
+__host__ __device__ constexpr float prefix_delta(int r) {
+  return (float)((1 << (8 - r)) - 1) * 0.5f;
+}
+
+__device__ __forceinline__ float h2f(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// Round-to-nearest-even fp32 -> bf16 for finite values.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  f16x2 v = {(_Float16)a, (_Float16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+struct PlanePtrs {
+  const uint32_t* p[kPlanes];
+};
+
+// word offset of (row, unit) in plane p
+__device__ __forceinline__ size_t plane_word(int p, size_t row, size_t unit, size_t units_per_row) {
+  return (row * units_per_row + unit) * (size_t)kPlaneBits[p];
+}
+
+}  // namespace mq

@@ -1,0 +1,375 @@
+// mq_gemm.hip -- MFMA path for m > 4 (skinny decode batches and prefill).
+//
+// Y[m, n] = sum_k X[m, k] * w_hat[n, k].  Per 64-wide k step a workgroup
+//  * copies its X tile (BM x 64, fp16/bf16) global -> VGPR -> LDS,
+//  * loads the packed planes of its weight tile (BN rows x two 32-code units),
+//    rebuilds and slices the codes in VGPRs and dequantizes them exactly in
+//    fp32 (w_hat = v*s + (delta - z)*s, all terms exact for an fp16 scale and
+//    an integer zero point), rounds once to the activation dtype and writes
+//    the tile to LDS,
+//  * runs v_mfma_f32_16x16x32_{bf16,f16} from LDS with fp32 accumulators.
+// LDS is double buffered: the next step's global loads are issued before the
+// current step's MFMAs and its dequantization is written to the other buffer
+// afterwards, so one barrier per step suffices.
+//
+// This is the pages' fused dequantize-and-multiply design for prefill and
+// larger batches (MatGPTQ "Efficient and Accurate Inference over Nested
+// Quantized Models", section 4: on-the-fly dequantization, fp32
+// accumulation; prefill support, contribution 3) mapped onto gfx950 matrix
+// cores: tiles are multiples of the 16x16x32 MFMA block, a wave owns a
+// (BM/WM) x (BN/WN) sub-tile, and workgroups that share weight tiles are
+// placed on the same XCD so the tiles are read from one L2.
+//
+// Split-k (when the caller provides a workspace): blockIdx.y selects a k
+// range, partial tiles go to workspace[split][m][n] in fp32, and a second
+// kernel sums the splits in a fixed order, so results stay deterministic.
+#include "mq_common.h"
+#include "mq_kernels.h"
+
+namespace mq {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
+constexpr int BK = 64;
+constexpr int LDS_PAD = 8;  // 16-bit elements of padding per LDS row
+constexpr int LDS_ROW = BK + LDS_PAD;
+
+struct GemmArgs {
+  const void* x;
+  void* y;        // [m, n] in x's dtype, or fp32 workspace [splits][m][n]
+  PlanePtrs pl;
+  const uint16_t* scales;
+  const uint16_t* zeros;
+  int m, n, k, group;
+  int tiles_m, tiles_n;
+  int ksteps_per_split;
+  int to_workspace;
+};
+
+template <int BF16>
+__device__ __forceinline__ floatx4 mfma16x16x32(const uint4& a, const uint4& b, const floatx4& c) {
+  if constexpr (BF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+}
+
+template <int R, int ROUND, int BF16, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs a) {
+  constexpr int T = 64 * WM * WN;
+  constexpr int NP = planes_needed(R, ROUND);
+  constexpr int FM = BM / WM / 16;
+  constexpr int FN = BN / WN / 16;
+  constexpr int CX = (BM * 8 + T - 1) / T;  // 16-byte X chunks per thread per step
+  constexpr int CW = BN * 2 / T;             // (row, unit) weight items per thread per step
+  static_assert(CW >= 1 && CW * T == BN * 2, "W tile split");
+  constexpr float kDelta = ROUND ? 0.0f : prefix_delta(R);
+
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM][LDS_ROW];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN][LDS_ROW];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave % WM, wn = wave / WM;
+
+  // ---- tile selection: workgroups sharing a weight tile land on one XCD ----
+  const int G = a.tiles_m * a.tiles_n;
+  int logical = blockIdx.x;
+  if ((G & 7) == 0) logical = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  const int tm = logical % a.tiles_m, tn = logical / a.tiles_m;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const int KT = a.k / BK;
+  const int kt_begin = blockIdx.y * a.ksteps_per_split;
+  const int kt_end = min(KT, kt_begin + a.ksteps_per_split);
+
+  const size_t upr = (size_t)(a.k >> 5);
+  const int gpr = a.k / a.group;
+  const uint16_t* xg = static_cast<const uint16_t*>(a.x);
+
+  uint4 xreg[CX];
+  uint32_t wrec[CW][kUnitWords];
+  uint16_t sraw[CW], zraw[CW];
+
+  auto load_global = [&](int kt) {
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int i = 0; i < CX; ++i) {
+      const int c = tid + i * T;
+      const int row = c >> 3, col = (c & 7) * 8;
+      const int mrow = m0 + row;
+      xreg[i] = (c < BM * 8 && mrow < a.m)
+                    ? *reinterpret_cast<const uint4*>(xg + (size_t)mrow * a.k + k0 + col)
+                    : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < CW; ++i) {
+      const int it = tid + i * T;
+      const int row = it >> 1, u = it & 1;
+      int nrow = n0 + row;
+      if (nrow >= a.n) nrow = a.n - 1;  // clamped load; the output column is never stored
+      const size_t unit = (size_t)nrow * upr + (size_t)(kt * 2 + u);
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        if (kPlaneBits[p] == 2) {
+          uint2 v = reinterpret_cast<const uint2*>(a.pl.p[p])[unit];
+          wrec[i][kUnitOff[p]] = v.x;
+          wrec[i][kUnitOff[p] + 1] = v.y;
+        } else {
+          wrec[i][kUnitOff[p]] = a.pl.p[p][unit];
+        }
+      }
+      const size_t g = (size_t)nrow * gpr + (size_t)(k0 / a.group);
+      sraw[i] = a.scales[g];
+      zraw[i] = a.zeros[g];
+    }
+  };
+
+  auto store_lds = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < CX; ++i) {
+      const int c = tid + i * T;
+      const int row = c >> 3, col = (c & 7) * 8;
+      if (c < BM * 8) *reinterpret_cast<uint4*>(&As[buf][row][col]) = xreg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < CW; ++i) {
+      const int it = tid + i * T;
+      const int row = it >> 1, u = it & 1;
+      const float s = h2f(sraw[i]);
+      const float cz = (kDelta - h2f(zraw[i])) * s;  // exact
+      uint32_t bytes[8];
+      bytes[0] = assemble_word<NP, 0>(wrec[i]);
+      bytes[1] = assemble_word<NP, 1>(wrec[i]);
+      bytes[2] = assemble_word<NP, 2>(wrec[i]);
+      bytes[3] = assemble_word<NP, 3>(wrec[i]);
+      bytes[4] = assemble_word<NP, 4>(wrec[i]);
+      bytes[5] = assemble_word<NP, 5>(wrec[i]);
+      bytes[6] = assemble_word<NP, 6>(wrec[i]);
+      bytes[7] = assemble_word<NP, 7>(wrec[i]);
+      uint32_t h[16];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t v = slice_bytes<R, ROUND>(bytes[j]);
+        const float w0 = fmaf((float)(v & 0xFFu), s, cz);
+        const float w1 = fmaf((float)((v >> 8) & 0xFFu), s, cz);
+        const float w2 = fmaf((float)((v >> 16) & 0xFFu), s, cz);
+        const float w3 = fmaf((float)(v >> 24), s, cz);
+        h[2 * j] = BF16 ? pack_bf16x2(w0, w1) : pack_f16x2(w0, w1);
+        h[2 * j + 1] = BF16 ? pack_bf16x2(w2, w3) : pack_f16x2(w2, w3);
+      }
+      uint4* dst = reinterpret_cast<uint4*>(&Bs[buf][row][u * 32]);
+      dst[0] = make_uint4(h[0], h[1], h[2], h[3]);
+      dst[1] = make_uint4(h[4], h[5], h[6], h[7]);
+      dst[2] = make_uint4(h[8], h[9], h[10], h[11]);
+      dst[3] = make_uint4(h[12], h[13], h[14], h[15]);
+    }
+  };
+
+  floatx4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const int arow = wm * (BM / WM) + (lane & 15);
+  const int brow = wn * (BN / WN) + (lane & 15);
+  const int kq = (lane >> 4) * 8;
+
+  if (kt_begin < kt_end) {
+    load_global(kt_begin);
+    store_lds(0);
+    __syncthreads();
+    for (int kt = kt_begin; kt < kt_end; ++kt) {
+      const int cur = (kt - kt_begin) & 1;
+      const bool has_next = kt + 1 < kt_end;
+      if (has_next) load_global(kt + 1);
+#pragma unroll
+      for (int kk = 0; kk < BK; kk += 32) {
+        uint4 af[FM], bfr[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const uint4*>(&As[cur][arow + i * 16][kk + kq]);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bfr[j] = *reinterpret_cast<const uint4*>(&Bs[cur][brow + j * 16][kk + kq]);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) acc[i][j] = mfma16x16x32<BF16>(af[i], bfr[j], acc[i][j]);
+      }
+      if (has_next) store_lds(cur ^ 1);
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue: lane holds D[4*(lane/16) + v][lane % 16] of each block ----
+  const int mbase = m0 + wm * (BM / WM) + (lane >> 4) * 4;
+  const int nbase = n0 + wn * (BN / WN) + (lane & 15);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int n = nbase + j * 16;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = mbase + i * 16 + v;
+        if (m < a.m && n < a.n) {
+          const float val = acc[i][j][v];
+          if (a.to_workspace) {
+            static_cast<float*>(a.y)[((size_t)blockIdx.y * a.m + m) * a.n + n] = val;
+          } else {
+            uint16_t* y = static_cast<uint16_t*>(a.y) + (size_t)m * a.n + n;
+            *y = (uint16_t)((BF16 ? pack_bf16x2(val, 0.f) : pack_f16x2(val, 0.f)) & 0xFFFFu);
+          }
+        }
+      }
+    }
+  }
+}
+
+// Fixed-order sum of the split-k partials, then one rounding to the output dtype.
+template <int BF16>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws, int splits, size_t mn,
+                                                            uint16_t* __restrict__ y) {
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= mn) return;
+  float t = 0.f;
+  for (int s = 0; s < splits; ++s) t += ws[(size_t)s * mn + i];
+  y[i] = (uint16_t)((BF16 ? pack_bf16x2(t, 0.f) : pack_f16x2(t, 0.f)) & 0xFFFFu);
+}
+
+// ----------------------------------------------------------------------------
+// tile configurations and planning
+// ----------------------------------------------------------------------------
+struct TileCfg {
+  int bm, bn;
+};
+constexpr TileCfg kCfgs[] = {
+    {256, 256},  // 0: prefill, 8 waves (2 x 4), wave tile 128 x 64
+    {128, 256},  // 1: 8 waves (2 x 4), wave tile 64 x 64
+    {64, 256},   // 2: 4 waves (1 x 4), wave tile 64 x 64
+    {32, 256},   // 3: 4 waves (1 x 4), wave tile 32 x 64
+    {16, 256},   // 4: 4 waves (1 x 4), wave tile 16 x 64
+    {128, 128},  // 5: 4 waves (2 x 2), wave tile 64 x 64
+};
+constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
+constexpr int kCUs = 256;
+constexpr int kMaxSplits = 16;
+
+static inline int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
+
+static int tiles_of(int cfg, int m, int n) { return cdiv(m, kCfgs[cfg].bm) * cdiv(n, kCfgs[cfg].bn); }
+
+static int pick_cfg(int m, int n) {
+  if (m <= 16) return 4;
+  if (m <= 32) return 3;
+  if (m <= 64) return 2;
+  if (m <= 128) return 1;
+  // large m: prefer 256x256 unless that leaves most CUs idle
+  const int t0 = tiles_of(0, m, n);
+  if (t0 >= kCUs) return 0;
+  return 5;
+}
+
+static int pick_splits(int cfg, int m, int n, int k) {
+  const int tiles = tiles_of(cfg, m, n);
+  const int KT = k / BK;
+  if (tiles >= kCUs) return 1;
+  int s = cdiv(kCUs, tiles);
+  if (s > kMaxSplits) s = kMaxSplits;
+  if (s > KT) s = KT;
+  // every split keeps at least 4 k steps
+  while (s > 1 && KT / s < 4) --s;
+  return s < 1 ? 1 : s;
+}
+
+size_t gemm_workspace_bytes(int m, int n, int k) {
+  if (m <= 0 || n <= 0 || k <= 0) return 0;
+  const int cfg = pick_cfg(m, n);
+  const int s = pick_splits(cfg, m, n, k);
+  return s > 1 ? (size_t)s * (size_t)m * (size_t)n * sizeof(float) : 0;
+}
+
+GemmPlan plan_gemm(int m, int n, int k, size_t workspace_bytes) {
+  GemmPlan p;
+  p.cfg = pick_cfg(m, n);
+  int s = pick_splits(p.cfg, m, n, k);
+  if (s > 1 && workspace_bytes < (size_t)s * (size_t)m * (size_t)n * sizeof(float)) s = 1;
+  p.splits = s;
+  return p;
+}
+
+template <int R, int ROUND, int BF16, int BM, int BN, int WM, int WN>
+static hipError_t gemm_launch_cfg(const GemmArgs& ga, int splits, hipStream_t s) {
+  dim3 grid((unsigned)(ga.tiles_m * ga.tiles_n), (unsigned)splits);
+  hipLaunchKernelGGL((gemm_kernel<R, ROUND, BF16, BM, BN, WM, WN>), grid, dim3(64 * WM * WN), 0, s, ga);
+  return hipGetLastError();
+}
+
+template <int R, int ROUND, int BF16>
+static hipError_t gemm_launch_t(const GemmArgs& ga, int cfg, int splits, hipStream_t s) {
+  switch (cfg) {
+    case 0: return gemm_launch_cfg<R, ROUND, BF16, 256, 256, 2, 4>(ga, splits, s);
+    case 1: return gemm_launch_cfg<R, ROUND, BF16, 128, 256, 2, 4>(ga, splits, s);
+    case 2: return gemm_launch_cfg<R, ROUND, BF16, 64, 256, 1, 4>(ga, splits, s);
+    case 3: return gemm_launch_cfg<R, ROUND, BF16, 32, 256, 1, 4>(ga, splits, s);
+    case 4: return gemm_launch_cfg<R, ROUND, BF16, 16, 256, 1, 4>(ga, splits, s);
+    default: return gemm_launch_cfg<R, ROUND, BF16, 128, 128, 2, 2>(ga, splits, s);
+  }
+}
+
+template <int R, int ROUND>
+static hipError_t gemm_launch_d(const GemmArgs& ga, int bf16, int cfg, int splits, hipStream_t s) {
+  return bf16 ? gemm_launch_t<R, ROUND, 1>(ga, cfg, splits, s) : gemm_launch_t<R, ROUND, 0>(ga, cfg, splits, s);
+}
+
+hipError_t launch_gemm(const LinearArgs& la, const GemmPlan& plan, void* workspace, hipStream_t s) {
+  GemmArgs ga;
+  ga.x = la.x;
+  ga.pl = la.pl;
+  ga.scales = la.scales;
+  ga.zeros = la.zeros;
+  ga.m = la.m;
+  ga.n = la.n;
+  ga.k = la.k;
+  ga.group = la.group;
+  ga.tiles_m = cdiv(la.m, kCfgs[plan.cfg].bm);
+  ga.tiles_n = cdiv(la.n, kCfgs[plan.cfg].bn);
+  const int KT = la.k / BK;
+  const int splits = plan.splits;
+  ga.ksteps_per_split = cdiv(KT, splits);
+  ga.to_workspace = splits > 1;
+  ga.y = splits > 1 ? workspace : la.y;
+  hipError_t e;
+#define MQ_GEMM_CASE(RR)                                                                   \
+  case RR:                                                                                 \
+    e = la.round_rule ? gemm_launch_d<RR, 1>(ga, la.bf16, plan.cfg, splits, s)             \
+                      : gemm_launch_d<RR, 0>(ga, la.bf16, plan.cfg, splits, s);            \
+    break;
+  switch (la.r) {
+    MQ_GEMM_CASE(2)
+    MQ_GEMM_CASE(3)
+    MQ_GEMM_CASE(4)
+    MQ_GEMM_CASE(6)
+    MQ_GEMM_CASE(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef MQ_GEMM_CASE
+  if (e != hipSuccess || splits == 1) return e;
+  const size_t mn = (size_t)la.m * (size_t)la.n;
+  const unsigned blocks = (unsigned)((mn + 255) / 256);
+  if (la.bf16)
+    hipLaunchKernelGGL(splitk_reduce_kernel<1>, dim3(blocks), dim3(256), 0, s, static_cast<const float*>(workspace),
+                       splits, mn, static_cast<uint16_t*>(la.y));
+  else
+    hipLaunchKernelGGL(splitk_reduce_kernel<0>, dim3(blocks), dim3(256), 0, s, static_cast<const float*>(workspace),
+                       splits, mn, static_cast<uint16_t*>(la.y));
+  return hipGetLastError();
+}
+
+}  // namespace mq
