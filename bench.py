@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Benchmark of the sliced-precision quantized linear layer on one MI355X.
+
+Workload (one step): the Llama-3.1-8B FFN projections (gate and up 4096->14336,
+down 14336->4096) at decode batch M = 1, fp16 activations, one int8 parent
+per matrix (g = 128, fp16 scale/zero, W ~ N(0, 0.02^2) with 0.1% outliers x10),
+sliced with the true-prefix rule at every width r in {2, 3, 4, 6, 8}: 15 layer
+calls, issued as one mixed-width call per width.
+
+Inputs are resident in HBM before timing.  Each step reads a different copy of
+the parents from a ring whose bytes read per pass exceed the 256 MB MALL, so
+weight reads come from HBM, not the last-level cache.
+
+Printed JSON (one line): value = algorithmic bytes of all calls / wall time of
+the timed steps (GB/s).  Algorithmic bytes per call = bit planes the width
+reads + 4 B (fp16 scale + zero) per group + X (2*M*K) + Y (2*M*N).
+`roofline` is for the kernel that takes the most time per step (the r = 8
+decode GEMV): its bytes per launch over its average launch duration, measured
+with HIP events on the launch stream during the timed steps.  `per_r` gives
+the same figure for every width.  `prefill` times the M = 2048 bf16 prefill
+GEMM (same shapes, r in {2, 4, 8}) against the dense bf16 MFMA peak.
+`cpu_baseline` times the CPU oracle on one matrix at every width.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+WIDTHS = (2, 3, 4, 6, 8)
+PREFILL_WIDTHS = (2, 4, 8)
+GROUP = 128
+METRIC = "sliced W·X: decode GB/s (packed bytes, %HBM peak) + prefill TFLOP/s (%MFMA) per r"
+PLANE_BITS = (2, 1, 1, 2, 2)
+PLANES_FOR_R = {2: 1, 3: 2, 4: 3, 6: 4, 8: 5}
+DECODE_KERNEL_SRC = os.path.join(ROOT, "nested_integer_weight_amd", "csrc", "mq_gemv.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_r8_llama8b_ffn_m1.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def alg_bytes(m, n, k, r, group=GROUP):
+    planes = sum(n * k * PLANE_BITS[p] // 8 for p in range(PLANES_FOR_R[r]))
+    return planes + 4 * n * (k // group) + 2 * m * k + 2 * m * n
+
+
+def src_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--ring", type=int, default=8, help="distinct parent copies cycled through")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill GEMM lines")
+    ap.add_argument("--prefill-iters", type=int, default=10)
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="also run one device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (this build has no "
+              "multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from nested_integer_weight_amd import mq, synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    # ---------------- inputs (resident before timing) ----------------
+    mats = []
+    for tid, (name, n, k) in enumerate(synth.LLAMA8B_FFN):
+        t0 = time.time()
+        lay = synth.make_layer(cfg_id=2, tensor_id=tid, n=n, k=k, m=0, group=GROUP, outlier_frac=1e-3)
+        x = synth.activations(synth.rng_for(2, 100 + tid), 1, k, "f16")
+        q = torch.from_numpy(lay.q).to(dev)
+        s = torch.from_numpy(lay.scales).to(dev)
+        z = torch.from_numpy(lay.zeros).to(dev)
+        base = mq.pack_parent(q)
+        copies = []
+        for c in range(args.ring):
+            planes = [p.clone() for p in base.planes]
+            copies.append((mq.Packed(n, k, planes), s.clone(), z.clone()))
+        del q
+        mats.append(dict(name=name, n=n, k=k, lay=lay, x=x, xd=x.to(dev), copies=copies,
+                         y=torch.empty((1, n), dtype=torch.float16, device=dev)))
+        log(f"[bench] {name} {n}x{k}: parent packed, {args.ring} copies ({time.time() - t0:.1f}s)")
+    torch.cuda.synchronize()
+
+    def calls_for(step, r):
+        ri = WIDTHS.index(r)
+        c = (step * len(WIDTHS) + ri) % args.ring
+        out = []
+        for mt in mats:
+            pk, s, z = mt["copies"][c]
+            out.append(mq.Call(x=mt["xd"], packed=pk.truncated(r), r=r, rule="prefix", group=GROUP,
+                               scales=s, zeros=z, out=mt["y"]))
+        return out
+
+    bytes_r = {r: sum(alg_bytes(1, mt["n"], mt["k"], r) for mt in mats) for r in WIDTHS}
+    bytes_step = sum(bytes_r.values())
+    ring_bytes = sum(bytes_r.values()) * args.ring / len(WIDTHS) * len(WIDTHS)
+    log(f"[bench] bytes/step {bytes_step / 1e6:.1f} MB, ring pass {ring_bytes / 1e9:.2f} GB")
+
+    # ---------------- warmup ----------------
+    for i in range(args.warmup):
+        for r in WIDTHS:
+            mq.linear_mixed(calls_for(i, r))
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} steps done")
+
+    # ---------------- timed steps ----------------
+    ev = {r: [] for r in WIDTHS}
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step = args.warmup + i
+        for r in WIDTHS:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            mq.linear_mixed(calls_for(step, r))
+            e1.record(stream)
+            ev[r].append((e0, e1))
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    value = bytes_step * args.steps / (total_ms * 1e-3) / 1e9
+    log(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step, {value:.1f} GB/s")
+
+    per_r = {}
+    for r in WIDTHS:
+        ms = float(np.mean([a.elapsed_time(b) for a, b in ev[r]]))
+        per_launch_us = ms * 1e3 / len(mats)
+        b_launch = bytes_r[r] / len(mats)
+        gbs = b_launch / (per_launch_us * 1e-6) / 1e9
+        per_r[str(r)] = {"us_per_launch": round(per_launch_us, 3), "bytes_per_launch": int(b_launch),
+                         "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+    dom = per_r["8"]
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            t = json.load(open(TRAFFIC_FILE))
+            if t.get("kernel_src_sha256_16") == src_hash(DECODE_KERNEL_SRC):
+                traffic = t.get("hbm_bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    roofline = {"bound": "hbm", "achieved": dom["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(dom["GB/s"] / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "mq::gemv_kernel<r=8, prefix, m=1, fp16> (mq_linear decode path)",
+                "bytes_per_launch": dom["bytes_per_launch"], "us_per_launch": dom["us_per_launch"]}
+
+    # ---------------- prefill (M = 2048, bf16) ----------------
+    prefill = None
+    if not args.no_prefill:
+        prefill = {}
+        xs = {k: synth.activations(synth.rng_for(4, 7, k), 2048, k, "bf16").to(dev) for k in (4096, 14336)}
+        for r in PREFILL_WIDTHS:
+            rows = []
+            for mt in mats:
+                pk, s, z = mt["copies"][0]
+                x = xs[mt["k"]]
+                y = torch.empty((2048, mt["n"]), dtype=torch.bfloat16, device=dev)
+                for _ in range(2):
+                    mq.linear(x, pk, r, "prefix", GROUP, s, z, out=y)
+                torch.cuda.synchronize()
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                for _ in range(args.prefill_iters):
+                    mq.linear(x, pk, r, "prefix", GROUP, s, z, out=y)
+                b.record(stream)
+                torch.cuda.synchronize()
+                us = a.elapsed_time(b) * 1e3 / args.prefill_iters
+                flops = 2.0 * 2048 * mt["n"] * mt["k"]
+                rows.append((mt["name"], us, flops))
+            tot_us = sum(u for _, u, _ in rows)
+            tot_f = sum(f for _, _, f in rows)
+            tf = tot_f / (tot_us * 1e-6) / 1e12
+            prefill[str(r)] = {"TFLOP/s": round(tf, 1), "frac_mfma_bf16": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                               "us_per_matrix": {nm: round(u, 1) for nm, u, _ in rows}}
+            log(f"[bench] prefill r={r}: {tf:.1f} TFLOP/s")
+
+    if args.copy_calib_mib > 0:
+        nb = args.copy_calib_mib << 20
+        src = torch.empty(nb, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {nb} bytes done")
+
+    # ---------------- CPU oracle baseline ----------------
+    cpu = None
+    if not args.no_cpu:
+        from oracle import mq_oracle as O
+        try:
+            from threadpoolctl import threadpool_info
+            blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        except Exception:
+            blas_threads = 1
+        mt = mats[0]
+        lay = mt["lay"]
+        x64 = mt["x"].double().numpy()
+        t0 = time.perf_counter()
+        done = 0
+        for r in WIDTHS:
+            O.linear(x64, lay.q, lay.scales, lay.zeros, r, O.PREFIX, GROUP)
+            done += alg_bytes(1, mt["n"], mt["k"], r)
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(done / dt / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
+               "sample": f"oracle (numpy fp64 slice+dequant+matmul) on the gate matrix "
+                         f"{mt['n']}x{mt['k']} at M=1 for r in {list(WIDTHS)}: {dt:.1f} s"}
+        log(f"[bench] cpu oracle: {cpu['value']} GB/s in {dt:.1f}s")
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "llama3.1-8b-ffn decode: gate/up 4096->14336 + down 14336->4096, M=1, "
+                               "g=128, true-prefix, r in {2,3,4,6,8}",
+                   "global_batch": 1, "widths": list(WIDTHS), "ring_copies": args.ring},
+        "roofline": roofline,
+        "per_r": per_r,
+        "prefill": prefill,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -60,136 +60,250 @@ __device__ __forceinline__ void butterfly(float* acc, int lane) {
   }
 }
 
+// fp16 value of a 2-bit field that sits at mantissa bit P of each half of a
+// word: with exponent field 25 - P the half equals 2^(10 - P) + field.
+template <int P>
+__host__ __device__ constexpr uint32_t field2_magic() {
+  return ((25u - P) << 10) | ((25u - P) << 26);
+}
+// gfx9 VOP3 encodings take no literal and read at most one SGPR, so the
+// exponent pattern is kept in a VGPR and the mask in an SGPR: one v_and_or_b32.
+template <uint32_t C>
+__device__ __forceinline__ uint32_t vgpr_const() {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(C));
+  return r;
+}
+template <int P>
+__device__ __forceinline__ uint32_t field2_to_f16x2(uint32_t w, uint32_t magic_v) {
+  constexpr uint32_t mask = (3u << P) | (3u << (P + 16));
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "s"(mask), "v"(magic_v));
+  return r;
+}
+
+__device__ __forceinline__ float dot2h(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c, false);
+}
+
 template <int R, int ROUND, int MT, int BF16, int ROWS>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   constexpr int NP = planes_needed(R, ROUND);
-  constexpr int RB = (NP <= 2) ? ROWS : 4;  // rows whose loads are issued together
+  // width 2, true prefix, fp16: fields go straight from the plane-0 word to
+  // fp16 with one and-or per pair (no byte assembly)
+  constexpr bool FAST2 = (R == 2 && !ROUND && !BF16);
+  constexpr int RB = (NP <= 2) ? ROWS : 4;  // rows whose plane loads are in flight together
+  constexpr int NB = ROWS / RB;
+  static_assert(NB * RB == ROWS, "row batches");
   constexpr int V = ROWS * MT;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int slice = tid;  // a row spans the whole workgroup
   const int S = a.k >> 6;
-  const bool valid = slice < S;
-  const int slice_c = valid ? slice : 0;
-  const size_t upr = (size_t)(a.k >> 5);               // units per row
+  const bool valid = tid < S;            // one lane per 64-code slice; a row spans the workgroup
+  const int slice = valid ? tid : 0;
+  const size_t upr = (size_t)(a.k >> 5);  // units per row
   const int gpr = a.k / a.group;
-  const int gidx = (slice_c * 64) / a.group;
+  const int gidx = (slice * 64) / a.group;
   const size_t row0 = (size_t)blockIdx.x * (size_t)ROWS;
 
-  // ---- activations of this slice, once per workgroup ----
-  uint32_t xr[BF16 ? 1 : MT][32];
-  float xf[BF16 ? MT : 1][BF16 ? 64 : 1];
-  float xs[MT];
+  // ---- 1. issue the activation loads of this slice ----
+  // (unconditional loads from clamped addresses; invalid lanes/tokens are
+  // zeroed at first use so no load waits behind a branch)
+  uint4 xraw[MT][8];
 #pragma unroll
   for (int mm = 0; mm < MT; ++mm) {
-    const bool mok = valid && mm < a.m;
-    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) +
-                                                      (size_t)(mok ? mm : 0) * a.k + (size_t)slice_c * 64);
-    float sum = 0.f;
+    const int mc = mm < a.m ? mm : 0;
+    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + (size_t)mc * a.k +
+                                                      (size_t)slice * 64);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint4 v = mok ? src[i] : make_uint4(0, 0, 0, 0);
-      uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float lo, hi;
-        if constexpr (BF16) {
-          lo = __builtin_bit_cast(float, w4[j] << 16);
-          hi = __builtin_bit_cast(float, w4[j] & 0xFFFF0000u);
-          xf[mm][8 * i + 2 * j] = lo;
-          xf[mm][8 * i + 2 * j + 1] = hi;
-        } else {
-          xr[mm][4 * i + j] = w4[j];
-          f16x2_t h = __builtin_bit_cast(f16x2_t, w4[j]);
-          lo = (float)h.x;
-          hi = (float)h.y;
-        }
-        sum += lo + hi;
-      }
-    }
-    xs[mm] = sum;
+    for (int i = 0; i < 8; ++i) xraw[mm][i] = src[i];
   }
 
-  float acc[V];
-  constexpr float kDelta = ROUND ? 0.0f : prefix_delta(R);
-
-#pragma unroll
-  for (int i0 = 0; i0 < ROWS; i0 += RB) {
-    uint32_t rec[RB][2][kUnitWords];
-    uint16_t sraw[RB], zraw[RB];
+  // ---- 2. issue the plane loads of the first row batch ----
+  uint32_t rec[2][RB][2][kUnitWords];
+  uint16_t sraw[2][RB], zraw[2][RB];
+  auto load_batch = [&](int buf, int b) {
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
-      size_t row = row0 + (size_t)(i0 + i);
+      size_t row = row0 + (size_t)(b * RB + i);
       if (row >= (size_t)a.n) row = (size_t)a.n - 1;  // clamp loads; stores are guarded
-      const size_t unit = row * upr + (size_t)slice_c * 2;
+      const size_t unit = row * upr + (size_t)slice * 2;
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
         if (kPlaneBits[p] == 2) {
           uint4 v = *reinterpret_cast<const uint4*>(a.pl.p[p] + unit * 2);
-          rec[i][0][kUnitOff[p]] = v.x;
-          rec[i][0][kUnitOff[p] + 1] = v.y;
-          rec[i][1][kUnitOff[p]] = v.z;
-          rec[i][1][kUnitOff[p] + 1] = v.w;
+          rec[buf][i][0][kUnitOff[p]] = v.x;
+          rec[buf][i][0][kUnitOff[p] + 1] = v.y;
+          rec[buf][i][1][kUnitOff[p]] = v.z;
+          rec[buf][i][1][kUnitOff[p] + 1] = v.w;
         } else {
           uint2 v = *reinterpret_cast<const uint2*>(a.pl.p[p] + unit);
-          rec[i][0][kUnitOff[p]] = v.x;
-          rec[i][1][kUnitOff[p]] = v.y;
+          rec[buf][i][0][kUnitOff[p]] = v.x;
+          rec[buf][i][1][kUnitOff[p]] = v.y;
         }
       }
-      sraw[i] = a.scales[row * gpr + gidx];
-      zraw[i] = a.zeros[row * gpr + gidx];
+      sraw[buf][i] = a.scales[row * gpr + gidx];
+      zraw[buf][i] = a.zeros[row * gpr + gidx];
     }
+  };
+  load_batch(0, 0);
+
+  // ---- 3. activations: register layout, slice sums ----
+  constexpr uint32_t kOnes = 0x3C003C00u;  // (1.0, 1.0) in fp16
+  uint32_t xr[BF16 ? 1 : MT][32];           // fp16 pairs, natural k order or FAST2 pair order
+  float xf[BF16 ? MT : 1][BF16 ? 64 : 1];
+  float xs[MT];                             // sum of the slice's X
+  float xc[MT];                             // FAST2: sum of X times the fp16 field offsets
+#pragma unroll
+  for (int mm = 0; mm < MT; ++mm) {
+    const uint32_t keep = (valid && mm < a.m) ? 0xFFFFFFFFu : 0u;
+    uint32_t w[32];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      w[4 * i] = xraw[mm][i].x & keep;
+      w[4 * i + 1] = xraw[mm][i].y & keep;
+      w[4 * i + 2] = xraw[mm][i].z & keep;
+      w[4 * i + 3] = xraw[mm][i].w & keep;
+    }
+    if constexpr (BF16) {
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        xf[mm][2 * i] = __builtin_bit_cast(float, w[i] << 16);
+        xf[mm][2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u);
+        sum += xf[mm][2 * i] + xf[mm][2 * i + 1];
+      }
+      xs[mm] = sum;
+    } else {
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) sum = dot2h(w[i], kOnes, sum);
+      xs[mm] = sum;
+      if constexpr (FAST2) {
+        // pair idx of plane-0 word (u, d): (b, q) = (idx / 4, idx % 4) holds codes
+        // t0 = 32u + 16d + 4q + b (low half) and t0 + 2 (high half)
+        float c = 0.f;
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd) {
+#pragma unroll
+          for (int idx = 0; idx < 8; ++idx) {
+            const int b = idx / 4, q = idx % 4;
+            const int t0 = 16 * wd + 4 * q + b;
+            const uint32_t sel = (b == 0) ? 0x05040100u : 0x07060302u;
+            const uint32_t pr = __builtin_amdgcn_perm(w[t0 / 2 + 1], w[t0 / 2], sel);
+            xr[mm][8 * wd + idx] = pr;
+            const int P = 8 * b + 2 * q;
+            const int Pp = (idx < 5) ? P : P - 10;     // field bit after the optional shift by 10
+            const uint32_t off = (uint32_t)(25 - Pp) << 10;  // fp16 2^(10 - Pp)
+            c = dot2h(pr, off | (off << 16), c);
+          }
+        }
+        xc[mm] = c;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) xr[mm][i] = w[i];
+      }
+    }
+  }
+
+  float acc[V];
+  constexpr float kDelta = ROUND ? 0.0f : prefix_delta(R);
+  uint32_t mg0 = 0, mg2 = 0, mg4 = 0, mg6 = 0, mg8 = 0;
+  if constexpr (FAST2) {
+    mg0 = vgpr_const<field2_magic<0>()>();
+    mg2 = vgpr_const<field2_magic<2>()>();
+    mg4 = vgpr_const<field2_magic<4>()>();
+    mg6 = vgpr_const<field2_magic<6>()>();
+    mg8 = vgpr_const<field2_magic<8>()>();
+  }
+
+  // ---- 4. rows: batch b computes while batch b+1 is in flight ----
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int cur = b & 1;
+    if (b + 1 < NB) load_batch(cur ^ 1, b + 1);
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
       float dot[MT];
 #pragma unroll
       for (int mm = 0; mm < MT; ++mm) dot[mm] = 0.f;
+      if constexpr (FAST2) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        uint32_t bytes[8];
-        bytes[0] = assemble_word<NP, 0>(rec[i][u]);
-        bytes[1] = assemble_word<NP, 1>(rec[i][u]);
-        bytes[2] = assemble_word<NP, 2>(rec[i][u]);
-        bytes[3] = assemble_word<NP, 3>(rec[i][u]);
-        bytes[4] = assemble_word<NP, 4>(rec[i][u]);
-        bytes[5] = assemble_word<NP, 5>(rec[i][u]);
-        bytes[6] = assemble_word<NP, 6>(rec[i][u]);
-        bytes[7] = assemble_word<NP, 7>(rec[i][u]);
+        for (int wd = 0; wd < 4; ++wd) {
+          const uint32_t w = rec[cur][i][wd / 2][kUnitOff[0] + (wd & 1)];
+          const uint32_t ws = w >> 10;
+          uint32_t h[8];
+          h[0] = field2_to_f16x2<0>(w, mg0);
+          h[1] = field2_to_f16x2<2>(w, mg2);
+          h[2] = field2_to_f16x2<4>(w, mg4);
+          h[3] = field2_to_f16x2<6>(w, mg6);
+          h[4] = field2_to_f16x2<8>(w, mg8);
+          h[5] = field2_to_f16x2<0>(ws, mg0);
+          h[6] = field2_to_f16x2<2>(ws, mg2);
+          h[7] = field2_to_f16x2<4>(ws, mg4);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          if constexpr (BF16) {
-            uint32_t v = slice_bytes<R, ROUND>(bytes[j]);
+          for (int idx = 0; idx < 8; ++idx)
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-              float fv = (float)((v >> (8 * b)) & 0xFFu);
+            for (int mm = 0; mm < MT; ++mm) dot[mm] = dot2h(h[idx], xr[mm][8 * wd + idx], dot[mm]);
+        }
+      } else {
 #pragma unroll
-              for (int mm = 0; mm < MT; ++mm) dot[mm] = fmaf(fv, xf[mm][32 * u + 4 * j + b], dot[mm]);
-            }
-          } else {
-            uint32_t lo, hi;
-            if constexpr (ROUND && R < 8) {
-              slice_pairs<R, ROUND>(bytes[j], lo, hi);
-              lo |= 0x64006400u;
-              hi |= 0x64006400u;
+        for (int u = 0; u < 2; ++u) {
+          uint32_t bytes[8];
+          bytes[0] = assemble_word<NP, 0>(rec[cur][i][u]);
+          bytes[1] = assemble_word<NP, 1>(rec[cur][i][u]);
+          bytes[2] = assemble_word<NP, 2>(rec[cur][i][u]);
+          bytes[3] = assemble_word<NP, 3>(rec[cur][i][u]);
+          bytes[4] = assemble_word<NP, 4>(rec[cur][i][u]);
+          bytes[5] = assemble_word<NP, 5>(rec[cur][i][u]);
+          bytes[6] = assemble_word<NP, 6>(rec[cur][i][u]);
+          bytes[7] = assemble_word<NP, 7>(rec[cur][i][u]);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            if constexpr (BF16) {
+              const uint32_t v = slice_bytes<R, ROUND>(bytes[j]);
+#pragma unroll
+              for (int bb = 0; bb < 4; ++bb) {
+                const float fv = (float)((v >> (8 * bb)) & 0xFFu);
+#pragma unroll
+                for (int mm = 0; mm < MT; ++mm) dot[mm] = fmaf(fv, xf[mm][32 * u + 4 * j + bb], dot[mm]);
+              }
             } else {
-              lo = __builtin_amdgcn_perm(0x64646464u, bytes[j], 0x04010400u);
-              hi = __builtin_amdgcn_perm(0x64646464u, bytes[j], 0x04030402u);
-            }
-            const f16x2_t hl = __builtin_bit_cast(f16x2_t, lo);
-            const f16x2_t hh = __builtin_bit_cast(f16x2_t, hi);
+              uint32_t lo, hi;
+              if constexpr (ROUND && R < 8) {
+                slice_pairs<R, ROUND>(bytes[j], lo, hi);
+                lo |= 0x64006400u;
+                hi |= 0x64006400u;
+              } else {
+                // byte under an 0x64 exponent byte: the exact fp16 1024 + v
+                lo = __builtin_amdgcn_perm(0x64646464u, bytes[j], 0x04010400u);
+                hi = __builtin_amdgcn_perm(0x64646464u, bytes[j], 0x04030402u);
+              }
 #pragma unroll
-            for (int mm = 0; mm < MT; ++mm) {
-              dot[mm] = __builtin_amdgcn_fdot2(hl, __builtin_bit_cast(f16x2_t, xr[mm][16 * u + 2 * j]), dot[mm], false);
-              dot[mm] = __builtin_amdgcn_fdot2(hh, __builtin_bit_cast(f16x2_t, xr[mm][16 * u + 2 * j + 1]), dot[mm], false);
+              for (int mm = 0; mm < MT; ++mm) {
+                dot[mm] = dot2h(lo, xr[mm][16 * u + 2 * j], dot[mm]);
+                dot[mm] = dot2h(hi, xr[mm][16 * u + 2 * j + 1], dot[mm]);
+              }
             }
           }
         }
       }
-      const float s = h2f(sraw[i]);
-      const float c = (BF16 ? 0.0f : 1024.0f) + h2f(zraw[i]) - kDelta;
+      const float s = h2f(sraw[cur][i]);
+      const float z = h2f(zraw[cur][i]);
 #pragma unroll
-      for (int mm = 0; mm < MT; ++mm) acc[(i0 + i) * MT + mm] = valid ? s * fmaf(-c, xs[mm], dot[mm]) : 0.f;
+      for (int mm = 0; mm < MT; ++mm) {
+        float t;
+        if constexpr (FAST2) {
+          // sum_k X (2^(10-P) + f) - xc = sum_k X f;  v = 64 f
+          t = fmaf(64.0f, dot[mm] - xc[mm], (kDelta - z) * xs[mm]);
+        } else if constexpr (BF16) {
+          t = fmaf(kDelta - z, xs[mm], dot[mm]);
+        } else {
+          t = fmaf(-(1024.0f + z - kDelta), xs[mm], dot[mm]);
+        }
+        acc[(b * RB + i) * MT + mm] = valid ? s * t : 0.f;
+      }
     }
   }
 
