@@ -49,26 +49,35 @@ __device__ __forceinline__ uint32_t shift_signed(uint32_t v) {
   if constexpr (SH >= 0) return v << SH; else return v >> (-SH);
 }
 
-// Plane p's contribution to output word j (0..7) of a unit: the fields of
-// codes 4j..4j+3 moved to their code-bit position inside each byte.
+// (a & mask) | c in one v_and_or_b32: gfx9 VOP3 encodings take no literal, so
+// the mask is handed over in an SGPR and the accumulator stays in a VGPR.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(c));
+  return r;
+}
+
+// Plane P's word for output word J (codes 4J..4J+3 of a unit) shifted so the
+// four codes' fields sit at their code-bit position inside each byte.
 template <int P, int J>
-__device__ __forceinline__ uint32_t plane_part(const uint32_t* unit) {
+__device__ __forceinline__ uint32_t plane_shifted(const uint32_t* unit) {
   if constexpr (kPlaneBits[P] == 2) {
-    constexpr int q = J % 4;
-    constexpr int sh = kPlaneLsb[P] - 2 * q;
-    return shift_signed<sh>(unit[kUnitOff[P] + J / 4]) & rep4(3u << kPlaneLsb[P]);
+    return shift_signed<kPlaneLsb[P] - 2 * (J % 4)>(unit[kUnitOff[P] + J / 4]);
   } else {
-    constexpr int sh = kPlaneLsb[P] - J;
-    return shift_signed<sh>(unit[kUnitOff[P]]) & rep4(1u << kPlaneLsb[P]);
+    return shift_signed<kPlaneLsb[P] - J>(unit[kUnitOff[P]]);
   }
+}
+template <int P>
+__host__ __device__ constexpr uint32_t plane_mask() {
+  return rep4((kPlaneBits[P] == 2 ? 3u : 1u) << kPlaneLsb[P]);
 }
 
 template <int NP, int J, int P = 0>
-__device__ __forceinline__ uint32_t assemble_word_impl(const uint32_t* unit) {
+__device__ __forceinline__ uint32_t assemble_word_impl(const uint32_t* unit, uint32_t acc) {
   if constexpr (P >= NP) {
-    return 0u;
+    return acc;
   } else {
-    return plane_part<P, J>(unit) | assemble_word_impl<NP, J, P + 1>(unit);
+    return assemble_word_impl<NP, J, P + 1>(unit, and_or(plane_shifted<P, J>(unit), plane_mask<P>(), acc));
   }
 }
 
@@ -76,7 +85,7 @@ __device__ __forceinline__ uint32_t assemble_word_impl(const uint32_t* unit) {
 // the planes' bits in place and all lower bits zero.
 template <int NP, int J>
 __device__ __forceinline__ uint32_t assemble_word(const uint32_t* unit) {
-  return assemble_word_impl<NP, J>(unit);
+  return assemble_word_impl<NP, J, 1>(unit, plane_shifted<0, J>(unit) & plane_mask<0>());
 }
 
 // Byte-domain value of the r-bit slice for four codes packed in one word,

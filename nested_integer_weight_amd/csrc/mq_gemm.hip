@@ -23,6 +23,8 @@
 // Split-k (when the caller provides a workspace): blockIdx.y selects a k
 // range, partial tiles go to workspace[split][m][n] in fp32, and a second
 // kernel sums the splits in a fixed order, so results stay deterministic.
+#include <type_traits>
+
 #include "mq_common.h"
 #include "mq_kernels.h"
 
@@ -33,8 +35,10 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int BK = 64;
-constexpr int LDS_PAD = 8;  // 16-bit elements of padding per LDS row
-constexpr int LDS_ROW = BK + LDS_PAD;
+// LDS tiles are fragment-major: a 16-row x 32-k block is 1 KB and lane l of
+// an MFMA operand read owns bytes [16 l, 16 l + 16) of it (row 16b + l % 16,
+// k 8 (l / 16) .. + 7 of the block's k half).  Every fragment read and every
+// staging write is a contiguous 1 KB per wave: no bank conflicts, no padding.
 
 struct GemmArgs {
   const void* x;
@@ -59,19 +63,147 @@ __device__ __forceinline__ floatx4 mfma16x16x32(const uint4& a, const uint4& b, 
   }
 }
 
+// Per-thread state of one workgroup tile.  Helpers are force-inlined member
+// functions (not lambdas capturing arrays by reference), so the staging
+// arrays are scalarised into registers instead of living in memory.
+template <int R, int ROUND, int BF16, int BM, int BN, int WM, int WN>
+struct GemmTile {
+  static constexpr int T = 64 * WM * WN;
+  static constexpr int NP = planes_needed(R, ROUND);
+  static constexpr int FM = BM / WM / 16;
+  static constexpr int FN = BN / WN / 16;
+  static constexpr int CX = (BM * 8 + T - 1) / T;  // 16-byte X chunks per thread per step
+  static constexpr int CW = BN * 2 / T;             // (row, unit) weight items per thread per step
+  static_assert(CW >= 1 && CW * T == BN * 2, "W tile split");
+  static constexpr float kDelta = ROUND ? 0.0f : prefix_delta(R);
+
+  const GemmArgs& a;
+  int tid, m0, n0, gpr;
+  size_t upr;
+  // staging registers for the next k step
+  uint4 xreg[CX];
+  uint32_t wrec[CW][kUnitWords];
+  uint16_t sraw[CW], zraw[CW];
+  floatx4 acc[FM][FN];
+
+  __device__ __forceinline__ GemmTile(const GemmArgs& args, int t, int m0_, int n0_) : a(args), tid(t), m0(m0_), n0(n0_) {
+    upr = (size_t)(a.k >> 5);
+    gpr = a.k / a.group;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // X chunk c (16 B) is lane c % 64 of block c / 64 = (row16, k half):
+  // row 16 (c / 128) + c % 16, k 32 ((c / 64) % 2) + 8 ((c / 16) % 4).
+  // Unconditional loads from clamped addresses: X rows past m only feed
+  // output rows that are never stored.
+  __device__ __forceinline__ void load_x(int kt) {
+    const int k0 = kt * BK;
+    const uint16_t* xg = static_cast<const uint16_t*>(a.x);
+#pragma unroll
+    for (int i = 0; i < CX; ++i) {
+      const int c = (tid + i * T) % (BM * 8);
+      const int row = 16 * (c >> 7) + (c & 15);
+      const int col = 32 * ((c >> 6) & 1) + 8 * ((c >> 4) & 3);
+      const int mrow = min(m0 + row, a.m - 1);
+      xreg[i] = *reinterpret_cast<const uint4*>(xg + (size_t)mrow * a.k + k0 + col);
+    }
+  }
+  __device__ __forceinline__ void store_x(uint4* as) {
+#pragma unroll
+    for (int i = 0; i < CX; ++i) {
+      const int c = tid + i * T;
+      if ((BM * 8) % T == 0 || c < BM * 8) as[c] = xreg[i];
+    }
+  }
+  // weight item it -> (row it / 2, unit it % 2): a lane pair reads one row's two
+  // units, i.e. 16 contiguous bytes of a 2-bit plane
+  __device__ __forceinline__ void load_w(int kt) {
+    const int gk = (kt * BK) / a.group;
+#pragma unroll
+    for (int i = 0; i < CW; ++i) {
+      const int it = tid + i * T;
+      const int row = it >> 1, u = it & 1;
+      const int nrow = min(n0 + row, a.n - 1);  // clamped; the output column is never stored
+      const size_t unit = (size_t)nrow * upr + (size_t)(kt * 2 + u);
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        if (kPlaneBits[p] == 2) {
+          uint2 v = reinterpret_cast<const uint2*>(a.pl.p[p])[unit];
+          wrec[i][kUnitOff[p]] = v.x;
+          wrec[i][kUnitOff[p] + 1] = v.y;
+        } else {
+          wrec[i][kUnitOff[p]] = a.pl.p[p][unit];
+        }
+      }
+      const size_t g = (size_t)nrow * gpr + (size_t)gk;
+      sraw[i] = a.scales[g];
+      zraw[i] = a.zeros[g];
+    }
+  }
+  // rebuild, slice and dequantize (exactly, in fp32) the staged weights, round
+  // once to the MFMA dtype and write them to the LDS tile bs[BN/16][2][64]
+  __device__ __forceinline__ void store_w(uint4* bs) {
+#pragma unroll
+    for (int i = 0; i < CW; ++i) {
+      const int it = tid + i * T;
+      const int row = it >> 1, u = it & 1;
+      const float s = h2f(sraw[i]);
+      const float cz = (kDelta - h2f(zraw[i])) * s;  // exact
+      const uint32_t* rec = wrec[i];
+      uint32_t bytes[8];
+      bytes[0] = assemble_word<NP, 0>(rec);
+      bytes[1] = assemble_word<NP, 1>(rec);
+      bytes[2] = assemble_word<NP, 2>(rec);
+      bytes[3] = assemble_word<NP, 3>(rec);
+      bytes[4] = assemble_word<NP, 4>(rec);
+      bytes[5] = assemble_word<NP, 5>(rec);
+      bytes[6] = assemble_word<NP, 6>(rec);
+      bytes[7] = assemble_word<NP, 7>(rec);
+      uint32_t h[16];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t v = slice_bytes<R, ROUND>(bytes[j]);
+        const float w0 = fmaf((float)(v & 0xFFu), s, cz);
+        const float w1 = fmaf((float)((v >> 8) & 0xFFu), s, cz);
+        const float w2 = fmaf((float)((v >> 16) & 0xFFu), s, cz);
+        const float w3 = fmaf((float)(v >> 24), s, cz);
+        h[2 * j] = BF16 ? pack_bf16x2(w0, w1) : pack_f16x2(w0, w1);
+        h[2 * j + 1] = BF16 ? pack_bf16x2(w2, w3) : pack_f16x2(w2, w3);
+      }
+      // 8-k chunk j of this row's k half u is lane (row % 16) + 16 j of block (row / 16, u)
+      uint4* dst = bs + ((row >> 4) * 2 + u) * 64 + (row & 15);
+      dst[0] = make_uint4(h[0], h[1], h[2], h[3]);
+      dst[16] = make_uint4(h[4], h[5], h[6], h[7]);
+      dst[32] = make_uint4(h[8], h[9], h[10], h[11]);
+      dst[48] = make_uint4(h[12], h[13], h[14], h[15]);
+    }
+  }
+  // MFMAs of one 32-wide k half from LDS tiles as[BM/16][2][64], bs[BN/16][2][64]
+  __device__ __forceinline__ void mma_half(const uint4* as, const uint4* bs, int kh, int lane, int wm, int wn) {
+    {
+      uint4 bfr[FN];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bfr[j] = bs[((wn * FN + j) * 2 + kh) * 64 + lane];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const uint4 af = as[((wm * FM + i) * 2 + kh) * 64 + lane];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma16x16x32<BF16>(af, bfr[j], acc[i][j]);
+      }
+    }
+  }
+};
+
 template <int R, int ROUND, int BF16, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs a) {
-  constexpr int T = 64 * WM * WN;
-  constexpr int NP = planes_needed(R, ROUND);
-  constexpr int FM = BM / WM / 16;
-  constexpr int FN = BN / WN / 16;
-  constexpr int CX = (BM * 8 + T - 1) / T;  // 16-byte X chunks per thread per step
-  constexpr int CW = BN * 2 / T;             // (row, unit) weight items per thread per step
-  static_assert(CW >= 1 && CW * T == BN * 2, "W tile split");
-  constexpr float kDelta = ROUND ? 0.0f : prefix_delta(R);
-
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM][LDS_ROW];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN][LDS_ROW];
+  using Tile = GemmTile<R, ROUND, BF16, BM, BN, WM, WN>;
+  constexpr int FM = Tile::FM, FN = Tile::FN;
+  // fragment-major LDS tiles, double buffered
+  __shared__ uint4 As[2][BM / 16 * 2 * 64];
+  __shared__ uint4 Bs[2][BN / 16 * 2 * 64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -89,120 +221,27 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs a) {
   const int kt_begin = blockIdx.y * a.ksteps_per_split;
   const int kt_end = min(KT, kt_begin + a.ksteps_per_split);
 
-  const size_t upr = (size_t)(a.k >> 5);
-  const int gpr = a.k / a.group;
-  const uint16_t* xg = static_cast<const uint16_t*>(a.x);
-
-  uint4 xreg[CX];
-  uint32_t wrec[CW][kUnitWords];
-  uint16_t sraw[CW], zraw[CW];
-
-  auto load_global = [&](int kt) {
-    const int k0 = kt * BK;
-#pragma unroll
-    for (int i = 0; i < CX; ++i) {
-      const int c = tid + i * T;
-      const int row = c >> 3, col = (c & 7) * 8;
-      const int mrow = m0 + row;
-      xreg[i] = (c < BM * 8 && mrow < a.m)
-                    ? *reinterpret_cast<const uint4*>(xg + (size_t)mrow * a.k + k0 + col)
-                    : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < CW; ++i) {
-      const int it = tid + i * T;
-      const int row = it >> 1, u = it & 1;
-      int nrow = n0 + row;
-      if (nrow >= a.n) nrow = a.n - 1;  // clamped load; the output column is never stored
-      const size_t unit = (size_t)nrow * upr + (size_t)(kt * 2 + u);
-#pragma unroll
-      for (int p = 0; p < NP; ++p) {
-        if (kPlaneBits[p] == 2) {
-          uint2 v = reinterpret_cast<const uint2*>(a.pl.p[p])[unit];
-          wrec[i][kUnitOff[p]] = v.x;
-          wrec[i][kUnitOff[p] + 1] = v.y;
-        } else {
-          wrec[i][kUnitOff[p]] = a.pl.p[p][unit];
-        }
-      }
-      const size_t g = (size_t)nrow * gpr + (size_t)(k0 / a.group);
-      sraw[i] = a.scales[g];
-      zraw[i] = a.zeros[g];
-    }
-  };
-
-  auto store_lds = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < CX; ++i) {
-      const int c = tid + i * T;
-      const int row = c >> 3, col = (c & 7) * 8;
-      if (c < BM * 8) *reinterpret_cast<uint4*>(&As[buf][row][col]) = xreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < CW; ++i) {
-      const int it = tid + i * T;
-      const int row = it >> 1, u = it & 1;
-      const float s = h2f(sraw[i]);
-      const float cz = (kDelta - h2f(zraw[i])) * s;  // exact
-      uint32_t bytes[8];
-      bytes[0] = assemble_word<NP, 0>(wrec[i]);
-      bytes[1] = assemble_word<NP, 1>(wrec[i]);
-      bytes[2] = assemble_word<NP, 2>(wrec[i]);
-      bytes[3] = assemble_word<NP, 3>(wrec[i]);
-      bytes[4] = assemble_word<NP, 4>(wrec[i]);
-      bytes[5] = assemble_word<NP, 5>(wrec[i]);
-      bytes[6] = assemble_word<NP, 6>(wrec[i]);
-      bytes[7] = assemble_word<NP, 7>(wrec[i]);
-      uint32_t h[16];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t v = slice_bytes<R, ROUND>(bytes[j]);
-        const float w0 = fmaf((float)(v & 0xFFu), s, cz);
-        const float w1 = fmaf((float)((v >> 8) & 0xFFu), s, cz);
-        const float w2 = fmaf((float)((v >> 16) & 0xFFu), s, cz);
-        const float w3 = fmaf((float)(v >> 24), s, cz);
-        h[2 * j] = BF16 ? pack_bf16x2(w0, w1) : pack_f16x2(w0, w1);
-        h[2 * j + 1] = BF16 ? pack_bf16x2(w2, w3) : pack_f16x2(w2, w3);
-      }
-      uint4* dst = reinterpret_cast<uint4*>(&Bs[buf][row][u * 32]);
-      dst[0] = make_uint4(h[0], h[1], h[2], h[3]);
-      dst[1] = make_uint4(h[4], h[5], h[6], h[7]);
-      dst[2] = make_uint4(h[8], h[9], h[10], h[11]);
-      dst[3] = make_uint4(h[12], h[13], h[14], h[15]);
-    }
-  };
-
-  floatx4 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  const int arow = wm * (BM / WM) + (lane & 15);
-  const int brow = wn * (BN / WN) + (lane & 15);
-  const int kq = (lane >> 4) * 8;
+  Tile t(a, tid, m0, n0);
 
   if (kt_begin < kt_end) {
-    load_global(kt_begin);
-    store_lds(0);
+    t.load_w(kt_begin);
+    t.load_x(kt_begin);
+    t.store_x(As[0]);
+    t.store_w(Bs[0]);
     __syncthreads();
     for (int kt = kt_begin; kt < kt_end; ++kt) {
       const int cur = (kt - kt_begin) & 1;
       const bool has_next = kt + 1 < kt_end;
-      if (has_next) load_global(kt + 1);
-#pragma unroll
-      for (int kk = 0; kk < BK; kk += 32) {
-        uint4 af[FM], bfr[FN];
-#pragma unroll
-        for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const uint4*>(&As[cur][arow + i * 16][kk + kq]);
-#pragma unroll
-        for (int j = 0; j < FN; ++j) bfr[j] = *reinterpret_cast<const uint4*>(&Bs[cur][brow + j * 16][kk + kq]);
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j) acc[i][j] = mfma16x16x32<BF16>(af[i], bfr[j], acc[i][j]);
+      if (has_next) {  // next step's loads are in flight during this step's MFMAs
+        t.load_x(kt + 1);
+        t.load_w(kt + 1);
       }
-      if (has_next) store_lds(cur ^ 1);
+      t.mma_half(As[cur], Bs[cur], 0, lane, wm, wn);
+      t.mma_half(As[cur], Bs[cur], 1, lane, wm, wn);
+      if (has_next) {
+        t.store_x(As[cur ^ 1]);
+        t.store_w(Bs[cur ^ 1]);
+      }
       __syncthreads();
     }
   }
@@ -219,7 +258,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs a) {
       for (int v = 0; v < 4; ++v) {
         const int m = mbase + i * 16 + v;
         if (m < a.m && n < a.n) {
-          const float val = acc[i][j][v];
+          const float val = t.acc[i][j][v];
           if (a.to_workspace) {
             static_cast<float*>(a.y)[((size_t)blockIdx.y * a.m + m) * a.n + n] = val;
           } else {
@@ -256,6 +295,7 @@ constexpr TileCfg kCfgs[] = {
     {32, 256},   // 3: 4 waves (1 x 4), wave tile 32 x 64
     {16, 256},   // 4: 4 waves (1 x 4), wave tile 16 x 64
     {128, 128},  // 5: 4 waves (2 x 2), wave tile 64 x 64
+    {256, 128},  // 6: 4 waves (2 x 2), wave tile 128 x 64 (accumulators in AGPRs)
 };
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 constexpr int kCUs = 256;
@@ -319,7 +359,8 @@ static hipError_t gemm_launch_t(const GemmArgs& ga, int cfg, int splits, hipStre
     case 2: return gemm_launch_cfg<R, ROUND, BF16, 64, 256, 1, 4>(ga, splits, s);
     case 3: return gemm_launch_cfg<R, ROUND, BF16, 32, 256, 1, 4>(ga, splits, s);
     case 4: return gemm_launch_cfg<R, ROUND, BF16, 16, 256, 1, 4>(ga, splits, s);
-    default: return gemm_launch_cfg<R, ROUND, BF16, 128, 128, 2, 2>(ga, splits, s);
+    case 5: return gemm_launch_cfg<R, ROUND, BF16, 128, 128, 2, 2>(ga, splits, s);
+    default: return gemm_launch_cfg<R, ROUND, BF16, 256, 128, 2, 2>(ga, splits, s);
   }
 }
 

@@ -82,11 +82,26 @@ __device__ __forceinline__ uint32_t field2_to_f16x2(uint32_t w, uint32_t magic_v
   return r;
 }
 
+// value of quad lane t in every lane of the quad (DPP quad_perm [t,t,t,t]);
+// t is a constant after unrolling
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t v, int t) {
+  switch (t) {
+    case 0: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x00, 0xF, 0xF, false);
+    case 1: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x55, 0xF, 0xF, false);
+    case 2: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xAA, 0xF, 0xF, false);
+    default: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xFF, 0xF, 0xF, false);
+  }
+}
+
 __device__ __forceinline__ float dot2h(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c, false);
 }
 
-template <int R, int ROUND, int MT, int BF16, int ROWS>
+// SZ4 (group == 128, even groups per row): the scales and zeros of four rows
+// come in with one dword load per lane (quad lane t fetches the two groups of
+// its quad for row t) and DPP quad broadcasts hand every lane its own value;
+// otherwise each row costs two 16-bit loads per lane.
+template <int R, int ROUND, int MT, int BF16, int ROWS, int SZ4>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   constexpr int NP = planes_needed(R, ROUND);
   // width 2, true prefix, fp16: fields go straight from the plane-0 word to
@@ -122,7 +137,12 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
 
   // ---- 2. issue the plane loads of the first row batch ----
   uint32_t rec[2][RB][2][kUnitWords];
-  uint16_t sraw[2][RB], zraw[2][RB];
+  uint16_t sraw[2][SZ4 ? 1 : RB], zraw[2][SZ4 ? 1 : RB];
+  uint32_t sq[2][SZ4 ? RB / 4 : 1], zq[2][SZ4 ? RB / 4 : 1];
+  static_assert(!SZ4 || RB % 4 == 0, "quad scale loads need row batches of 4");
+  const int qgrp = ((tid >> 6) << 5) + 2 * (lane >> 2);       // first of the quad's two groups
+  const int qgrp_c = qgrp <= gpr - 2 ? qgrp : gpr - 2;          // clamp for idle lanes
+  const int sz_shift = 16 * ((lane >> 1) & 1);                  // this lane's half of the dword
   auto load_batch = [&](int buf, int b) {
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
@@ -143,8 +163,19 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
           rec[buf][i][1][kUnitOff[p]] = v.y;
         }
       }
-      sraw[buf][i] = a.scales[row * gpr + gidx];
-      zraw[buf][i] = a.zeros[row * gpr + gidx];
+      if constexpr (!SZ4) {
+        sraw[buf][i] = a.scales[row * gpr + gidx];
+        zraw[buf][i] = a.zeros[row * gpr + gidx];
+      }
+    }
+    if constexpr (SZ4) {
+#pragma unroll
+      for (int q = 0; q < RB / 4; ++q) {
+        size_t row = row0 + (size_t)(b * RB + 4 * q + (lane & 3));
+        if (row >= (size_t)a.n) row = (size_t)a.n - 1;
+        sq[buf][q] = *reinterpret_cast<const uint32_t*>(a.scales + row * gpr + qgrp_c);
+        zq[buf][q] = *reinterpret_cast<const uint32_t*>(a.zeros + row * gpr + qgrp_c);
+      }
     }
   };
   load_batch(0, 0);
@@ -289,8 +320,16 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
           }
         }
       }
-      const float s = h2f(sraw[cur][i]);
-      const float z = h2f(zraw[cur][i]);
+      float s, z;
+      if constexpr (SZ4) {
+        const uint32_t sd = quad_bcast(sq[cur][i / 4], i % 4);
+        const uint32_t zd = quad_bcast(zq[cur][i / 4], i % 4);
+        s = h2f((uint16_t)(sd >> sz_shift));
+        z = h2f((uint16_t)(zd >> sz_shift));
+      } else {
+        s = h2f(sraw[cur][i]);
+        z = h2f(zraw[cur][i]);
+      }
 #pragma unroll
       for (int mm = 0; mm < MT; ++mm) {
         float t;
@@ -363,7 +402,11 @@ static hipError_t gemv_launch_t(const LinearArgs& la, hipStream_t s) {
   const int threads = ((S + 63) / 64) * 64;  // one lane per 64-code slice, whole waves
   const unsigned blocks = (unsigned)((la.n + ROWS - 1) / ROWS);
   const size_t lds = (threads > 64) ? (size_t)(threads / 64) * ROWS * MT * sizeof(float) : 0;
-  hipLaunchKernelGGL((gemv_kernel<R, ROUND, MT, BF16, ROWS>), dim3(blocks), dim3(threads), lds, s, a);
+  const int gpr = la.k / la.group;
+  if (la.group == 128 && gpr % 2 == 0)
+    hipLaunchKernelGGL((gemv_kernel<R, ROUND, MT, BF16, ROWS, 1>), dim3(blocks), dim3(threads), lds, s, a);
+  else
+    hipLaunchKernelGGL((gemv_kernel<R, ROUND, MT, BF16, ROWS, 0>), dim3(blocks), dim3(threads), lds, s, a);
   return hipGetLastError();
 }
 
