@@ -310,21 +310,18 @@ static int pick_cfg(int m, int n) {
   if (m <= 32) return 3;
   if (m <= 64) return 2;
   if (m <= 128) return 1;
-  // large m: prefer 256x256 unless that leaves most CUs idle
-  const int t0 = tiles_of(0, m, n);
-  if (t0 >= kCUs) return 0;
-  return 5;
+  return 0;  // 256 x 256: half the dequantization per MAC of a 128-row tile
 }
 
+// Split k so that tiles x splits fills the CUs (at most 16 splits, at least 8
+// k steps each); 1 when the tiles alone fill the GPU.
 static int pick_splits(int cfg, int m, int n, int k) {
   const int tiles = tiles_of(cfg, m, n);
   const int KT = k / BK;
-  if (tiles >= kCUs) return 1;
+  if (tiles * 8 >= kCUs * 7) return 1;
   int s = cdiv(kCUs, tiles);
   if (s > kMaxSplits) s = kMaxSplits;
-  if (s > KT) s = KT;
-  // every split keeps at least 4 k steps
-  while (s > 1 && KT / s < 4) --s;
+  while (s > 1 && KT / s < 8) --s;
   return s < 1 ? 1 : s;
 }
 
@@ -338,9 +335,12 @@ size_t gemm_workspace_bytes(int m, int n, int k) {
 GemmPlan plan_gemm(int m, int n, int k, size_t workspace_bytes) {
   GemmPlan p;
   p.cfg = pick_cfg(m, n);
-  int s = pick_splits(p.cfg, m, n, k);
-  if (s > 1 && workspace_bytes < (size_t)s * (size_t)m * (size_t)n * sizeof(float)) s = 1;
-  p.splits = s;
+  p.splits = pick_splits(p.cfg, m, n, k);
+  if (p.splits > 1 && workspace_bytes < (size_t)p.splits * (size_t)m * (size_t)n * sizeof(float)) {
+    // no room to split: a smaller tile gives more workgroups instead
+    p.splits = 1;
+    if (p.cfg == 0 && tiles_of(0, m, n) * 8 < kCUs * 7) p.cfg = 5;
+  }
   return p;
 }
 

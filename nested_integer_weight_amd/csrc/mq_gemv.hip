@@ -107,7 +107,9 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   // width 2, true prefix, fp16: fields go straight from the plane-0 word to
   // fp16 with one and-or per pair (no byte assembly)
   constexpr bool FAST2 = (R == 2 && !ROUND && !BF16);
-  constexpr int RB = (NP <= 2) ? ROWS : 4;  // rows whose plane loads are in flight together
+  // rows per load batch: batch b + 1 is in flight while batch b is computed;
+  // small batches shorten the compute tail after the last bytes arrive
+  constexpr int RB = 2;
   constexpr int NB = ROWS / RB;
   static_assert(NB * RB == ROWS, "row batches");
   constexpr int V = ROWS * MT;
@@ -138,8 +140,8 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   // ---- 2. issue the plane loads of the first row batch ----
   uint32_t rec[2][RB][2][kUnitWords];
   uint16_t sraw[2][SZ4 ? 1 : RB], zraw[2][SZ4 ? 1 : RB];
-  uint32_t sq[2][SZ4 ? RB / 4 : 1], zq[2][SZ4 ? RB / 4 : 1];
-  static_assert(!SZ4 || RB % 4 == 0, "quad scale loads need row batches of 4");
+  uint32_t sq[SZ4 ? ROWS / 4 : 1], zq[SZ4 ? ROWS / 4 : 1];  // all rows' quads, loaded once
+  static_assert(!SZ4 || ROWS % 4 == 0, "quad scale loads cover rows in fours");
   const int qgrp = ((tid >> 6) << 5) + 2 * (lane >> 2);       // first of the quad's two groups
   const int qgrp_c = qgrp <= gpr - 2 ? qgrp : gpr - 2;          // clamp for idle lanes
   const int sz_shift = 16 * ((lane >> 1) & 1);                  // this lane's half of the dword
@@ -168,17 +170,17 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
         zraw[buf][i] = a.zeros[row * gpr + gidx];
       }
     }
-    if constexpr (SZ4) {
-#pragma unroll
-      for (int q = 0; q < RB / 4; ++q) {
-        size_t row = row0 + (size_t)(b * RB + 4 * q + (lane & 3));
-        if (row >= (size_t)a.n) row = (size_t)a.n - 1;
-        sq[buf][q] = *reinterpret_cast<const uint32_t*>(a.scales + row * gpr + qgrp_c);
-        zq[buf][q] = *reinterpret_cast<const uint32_t*>(a.zeros + row * gpr + qgrp_c);
-      }
-    }
   };
   load_batch(0, 0);
+  if constexpr (SZ4) {
+#pragma unroll
+    for (int q = 0; q < ROWS / 4; ++q) {
+      size_t row = row0 + (size_t)(4 * q + (lane & 3));
+      if (row >= (size_t)a.n) row = (size_t)a.n - 1;
+      sq[q] = *reinterpret_cast<const uint32_t*>(a.scales + row * gpr + qgrp_c);
+      zq[q] = *reinterpret_cast<const uint32_t*>(a.zeros + row * gpr + qgrp_c);
+    }
+  }
 
   // ---- 3. activations: register layout, slice sums ----
   constexpr uint32_t kOnes = 0x3C003C00u;  // (1.0, 1.0) in fp16
@@ -322,8 +324,9 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
       }
       float s, z;
       if constexpr (SZ4) {
-        const uint32_t sd = quad_bcast(sq[cur][i / 4], i % 4);
-        const uint32_t zd = quad_bcast(zq[cur][i / 4], i % 4);
+        const int ri = b * RB + i;  // row within the workgroup's block
+        const uint32_t sd = quad_bcast(sq[ri / 4], ri % 4);
+        const uint32_t zd = quad_bcast(zq[ri / 4], ri % 4);
         s = h2f((uint16_t)(sd >> sz_shift));
         z = h2f((uint16_t)(zd >> sz_shift));
       } else {
