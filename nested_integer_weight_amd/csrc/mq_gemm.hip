@@ -80,10 +80,11 @@ struct GemmTile {
   const GemmArgs& a;
   int tid, m0, n0, gpr;
   size_t upr;
-  // staging registers for the next k step
+  // staging registers: the X tile one k step ahead, the weight planes (from
+  // HBM, longer latency) two steps ahead in two slots
   uint4 xreg[CX];
-  uint32_t wrec[CW][kUnitWords];
-  uint16_t sraw[CW], zraw[CW];
+  uint32_t wrec[2][CW][kUnitWords];
+  uint16_t sraw[2][CW], zraw[2][CW];
   floatx4 acc[FM][FN];
 
   __device__ __forceinline__ GemmTile(const GemmArgs& args, int t, int m0_, int n0_) : a(args), tid(t), m0(m0_), n0(n0_) {
@@ -120,6 +121,7 @@ struct GemmTile {
   }
   // weight item it -> (row it / 2, unit it % 2): a lane pair reads one row's two
   // units, i.e. 16 contiguous bytes of a 2-bit plane
+  template <int SLOT>
   __device__ __forceinline__ void load_w(int kt) {
     const int gk = (kt * BK) / a.group;
 #pragma unroll
@@ -132,27 +134,28 @@ struct GemmTile {
       for (int p = 0; p < NP; ++p) {
         if (kPlaneBits[p] == 2) {
           uint2 v = reinterpret_cast<const uint2*>(a.pl.p[p])[unit];
-          wrec[i][kUnitOff[p]] = v.x;
-          wrec[i][kUnitOff[p] + 1] = v.y;
+          wrec[SLOT][i][kUnitOff[p]] = v.x;
+          wrec[SLOT][i][kUnitOff[p] + 1] = v.y;
         } else {
-          wrec[i][kUnitOff[p]] = a.pl.p[p][unit];
+          wrec[SLOT][i][kUnitOff[p]] = a.pl.p[p][unit];
         }
       }
       const size_t g = (size_t)nrow * gpr + (size_t)gk;
-      sraw[i] = a.scales[g];
-      zraw[i] = a.zeros[g];
+      sraw[SLOT][i] = a.scales[g];
+      zraw[SLOT][i] = a.zeros[g];
     }
   }
   // rebuild, slice and dequantize (exactly, in fp32) the staged weights, round
   // once to the MFMA dtype and write them to the LDS tile bs[BN/16][2][64]
+  template <int SLOT>
   __device__ __forceinline__ void store_w(uint4* bs) {
 #pragma unroll
     for (int i = 0; i < CW; ++i) {
       const int it = tid + i * T;
       const int row = it >> 1, u = it & 1;
-      const float s = h2f(sraw[i]);
-      const float cz = (kDelta - h2f(zraw[i])) * s;  // exact
-      const uint32_t* rec = wrec[i];
+      const float s = h2f(sraw[SLOT][i]);
+      const float cz = (kDelta - h2f(zraw[SLOT][i])) * s;  // exact
+      const uint32_t* rec = wrec[SLOT][i];
       uint32_t bytes[8];
       bytes[0] = assemble_word<NP, 0>(rec);
       bytes[1] = assemble_word<NP, 1>(rec);
@@ -224,25 +227,44 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs a) {
   Tile t(a, tid, m0, n0);
 
   if (kt_begin < kt_end) {
-    t.load_w(kt_begin);
+    const int klast = kt_end - 1;
+    t.template load_w<0>(kt_begin);
     t.load_x(kt_begin);
+    t.template load_w<1>(min(kt_begin + 1, klast));
     t.store_x(As[0]);
-    t.store_w(Bs[0]);
+    t.template store_w<0>(Bs[0]);
     __syncthreads();
-    for (int kt = kt_begin; kt < kt_end; ++kt) {
-      const int cur = (kt - kt_begin) & 1;
-      const bool has_next = kt + 1 < kt_end;
-      if (has_next) {  // next step's loads are in flight during this step's MFMAs
-        t.load_x(kt + 1);
-        t.load_w(kt + 1);
+    // Two k steps per trip so the LDS buffer and the weight staging slot are
+    // compile-time constants.  Step kt computes from buffer kt & 1, issues X
+    // for kt + 1 and weights for kt + 2 (into the slot that held kt), then
+    // writes step kt + 1 (X registers, weight slot loaded one trip earlier)
+    // into the other buffer.  Past the last step the loads repeat the last
+    // step (in bounds) and nothing more is stored.
+    for (int kt = kt_begin; kt < kt_end; kt += 2) {
+      {
+        const bool has_next = kt + 1 < kt_end;
+        if (has_next) t.load_x(kt + 1);
+        t.template load_w<0>(min(kt + 2, klast));
+        t.mma_half(As[0], Bs[0], 0, lane, wm, wn);
+        t.mma_half(As[0], Bs[0], 1, lane, wm, wn);
+        if (has_next) {
+          t.store_x(As[1]);
+          t.template store_w<1>(Bs[1]);
+        }
+        __syncthreads();
       }
-      t.mma_half(As[cur], Bs[cur], 0, lane, wm, wn);
-      t.mma_half(As[cur], Bs[cur], 1, lane, wm, wn);
-      if (has_next) {
-        t.store_x(As[cur ^ 1]);
-        t.store_w(Bs[cur ^ 1]);
+      if (kt + 1 < kt_end) {
+        const bool has_next = kt + 2 < kt_end;
+        if (has_next) t.load_x(kt + 2);
+        t.template load_w<1>(min(kt + 3, klast));
+        t.mma_half(As[1], Bs[1], 0, lane, wm, wn);
+        t.mma_half(As[1], Bs[1], 1, lane, wm, wn);
+        if (has_next) {
+          t.store_x(As[0]);
+          t.template store_w<0>(Bs[0]);
+        }
+        __syncthreads();
       }
-      __syncthreads();
     }
   }
 
