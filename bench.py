@@ -19,7 +19,12 @@ decode GEMV): its bytes per launch over its average launch duration, measured
 with HIP events on the launch stream during the timed steps.  `per_r` gives
 the same figure for every width.  `prefill` times the M = 2048 bf16 prefill
 GEMM (same shapes, r in {2, 4, 8}) against the dense bf16 MFMA peak.
-`cpu_baseline` times the CPU oracle on one matrix at every width.
+`skinny` times decode batches M in {8, 16, 32, 64} at r in {2, 3, 4, 8} on the
+same shapes against max(HBM time, MFMA time).  `mixnmatch` times one pass over
+42 Gemma-2-9B FFN blocks (gate/up 3584->14336, down 14336->3584, g = 128) with
+the seeded per-block widths (14 each of 2, 3 and 4 bits) at M = 1 (fp16) and
+M = 256 (bf16); those parents are drawn on the device (same recipe).
+`cpu_baseline` times the CPU oracle on all three matrices at every width.
 """
 from __future__ import annotations
 
@@ -68,8 +73,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--ring", type=int, default=8, help="distinct parent copies cycled through")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-steps", type=int, default=3, help="workload steps the CPU oracle baseline times")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill GEMM lines")
     ap.add_argument("--prefill-iters", type=int, default=10)
+    ap.add_argument("--no-skinny", action="store_true", help="skip the M in {8,16,32,64} lines")
+    ap.add_argument("--no-mix", action="store_true", help="skip the 42-block Mix'n'Match stack lines")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -205,6 +213,84 @@ def main():
                                "us_per_matrix": {nm: round(u, 1) for nm, u, _ in rows}}
             log(f"[bench] prefill r={r}: {tf:.1f} TFLOP/s")
 
+    # ---------------- skinny decode batches (M = 8..64, fp16) ----------------
+    skinny = None
+    if not args.no_skinny:
+        skinny = {}
+        for m in (8, 16, 32, 64):
+            xs_m = {k: synth.activations(synth.rng_for(3, m, k), m, k, "f16").to(dev) for k in (4096, 14336)}
+            ys_m = {n: torch.empty((m, n), dtype=torch.float16, device=dev) for n in (4096, 14336)}
+            for r in (2, 3, 4, 8):
+                def sk_calls(it):
+                    c = it % args.ring
+                    return [mq.Call(x=xs_m[mt["k"]], packed=mt["copies"][c][0].truncated(r), r=r, rule="prefix",
+                                    group=GROUP, scales=mt["copies"][c][1], zeros=mt["copies"][c][2],
+                                    out=ys_m[mt["n"]]) for mt in mats]
+                for i in range(3):
+                    mq.linear_mixed(sk_calls(i))
+                torch.cuda.synchronize()
+                iters = 2 * args.ring
+                a_ = torch.cuda.Event(enable_timing=True)
+                b_ = torch.cuda.Event(enable_timing=True)
+                a_.record(stream)
+                for i in range(iters):
+                    mq.linear_mixed(sk_calls(3 + i))
+                b_.record(stream)
+                torch.cuda.synchronize()
+                us = a_.elapsed_time(b_) * 1e3 / (iters * len(mats))
+                byt = sum(alg_bytes(m, mt["n"], mt["k"], r) for mt in mats) / len(mats)
+                fl = 2.0 * m * sum(mt["n"] * mt["k"] for mt in mats) / len(mats)
+                t_hbm = byt / (HBM_PEAK_GBS * 1e9)
+                t_mfma = fl / (BF16_MFMA_PEAK_TFLOPS * 1e12)
+                skinny[f"m{m}_r{r}"] = {"us_per_launch": round(us, 2), "GB/s": round(byt / (us * 1e-6) / 1e9, 1),
+                                        "TFLOP/s": round(fl / (us * 1e-6) / 1e12, 1),
+                                        "roofline_frac": round(max(t_hbm, t_mfma) / (us * 1e-6), 4)}
+            log(f"[bench] skinny m={m}: " + ", ".join(f"r{r} {skinny[f'm{m}_r{r}']['us_per_launch']}us"
+                                                       for r in (2, 3, 4, 8)))
+
+    # ---------------- Mix'n'Match stack: 42 Gemma-2-9B FFN blocks ----------------
+    mix = None
+    if not args.no_mix:
+        t0 = time.time()
+        widths = synth.mixnmatch_widths()
+        blocks = []
+        for blk in range(synth.GEMMA9B_BLOCKS):
+            for tid, (name, n, k) in enumerate(synth.GEMMA9B_FFN):
+                q, s_, z_ = synth.device_parent(1000 * (blk + 1) + tid, n, k, GROUP, dev)
+                pk = mq.pack_parent(q)
+                del q
+                blocks.append((blk, name, n, k, widths[blk], pk.truncated(widths[blk]), s_, z_))
+        torch.cuda.synchronize()
+        log(f"[bench] mixnmatch: {len(blocks)} parents drawn and packed ({time.time() - t0:.1f}s)")
+        mix = {"widths": widths, "mean_bits": sum(widths) / len(widths)}
+        for m, dt, tdt in ((1, "f16", torch.float16), (256, "bf16", torch.bfloat16)):
+            xk = {k: synth.activations(synth.rng_for(5, 77, k, m), m, k, dt).to(dev) for k in (3584, 14336)}
+            yn = {n: torch.empty((m, n), dtype=tdt, device=dev) for n in (3584, 14336)}
+            calls = [mq.Call(x=xk[k], packed=pk, r=r, rule="prefix", group=GROUP, scales=s_, zeros=z_, out=yn[n])
+                     for (blk, name, n, k, r, pk, s_, z_) in blocks]
+            mq.linear_mixed(calls)
+            torch.cuda.synchronize()
+            passes = 5 if m == 1 else 3
+            a_ = torch.cuda.Event(enable_timing=True)
+            b_ = torch.cuda.Event(enable_timing=True)
+            a_.record(stream)
+            for _ in range(passes):
+                mq.linear_mixed(calls)
+            b_.record(stream)
+            torch.cuda.synchronize()
+            us = a_.elapsed_time(b_) * 1e3 / passes
+            byt = sum(alg_bytes(m, n, k, r) for (blk, name, n, k, r, pk, s_, z_) in blocks)
+            fl = 2.0 * m * sum(n * k for (blk, name, n, k, r, pk, s_, z_) in blocks)
+            if m == 1:
+                mix["m1"] = {"us_per_pass": round(us, 1), "GB/s": round(byt / (us * 1e-6) / 1e9, 1),
+                             "frac_hbm": round(byt / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "bytes": int(byt)}
+            else:
+                mix["m256"] = {"us_per_pass": round(us, 1), "TFLOP/s": round(fl / (us * 1e-6) / 1e12, 1),
+                               "frac_mfma_bf16": round(fl / (us * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+                               "flop": fl}
+            log(f"[bench] mixnmatch m={m}: {us:.1f} us per pass of {len(blocks)} calls")
+        del blocks, calls
+
     if args.copy_calib_mib > 0:
         nb = args.copy_calib_mib << 20
         src = torch.empty(nb, dtype=torch.uint8, device=dev)
@@ -222,18 +308,20 @@ def main():
             blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
         except Exception:
             blas_threads = 1
-        mt = mats[0]
-        lay = mt["lay"]
-        x64 = mt["x"].double().numpy()
         t0 = time.perf_counter()
         done = 0
-        for r in WIDTHS:
-            O.linear(x64, lay.q, lay.scales, lay.zeros, r, O.PREFIX, GROUP)
-            done += alg_bytes(1, mt["n"], mt["k"], r)
+        for _ in range(args.cpu_steps):
+            for mt in mats:
+                lay = mt["lay"]
+                x64 = mt["x"].double().numpy()
+                for r in WIDTHS:
+                    O.linear(x64, lay.q, lay.scales, lay.zeros, r, O.PREFIX, GROUP)
+                    done += alg_bytes(1, mt["n"], mt["k"], r)
         dt = time.perf_counter() - t0
         cpu = {"value": round(done / dt / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
-               "sample": f"oracle (numpy fp64 slice+dequant+matmul) on the gate matrix "
-                         f"{mt['n']}x{mt['k']} at M=1 for r in {list(WIDTHS)}: {dt:.1f} s"}
+               "sample": f"oracle (numpy fp64 slice + dequant + matmul) on {args.cpu_steps} steps of the "
+                         f"workload: gate, up and down at M=1 for r in {list(WIDTHS)} "
+                         f"({15 * args.cpu_steps} calls), {dt:.1f} s"}
         log(f"[bench] cpu oracle: {cpu['value']} GB/s in {dt:.1f}s")
 
     out = {
@@ -246,6 +334,8 @@ def main():
         "roofline": roofline,
         "per_r": per_r,
         "prefill": prefill,
+        "skinny": skinny,
+        "mixnmatch": mix,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -128,3 +128,31 @@ def mixnmatch_widths(n_blocks: int = GEMMA9B_BLOCKS, seed: int = 0) -> list[int]
     per = n_blocks // 3
     base = np.array([2] * per + [3] * per + [4] * (n_blocks - 2 * per))
     return [int(v) for v in np.random.default_rng(seed).permutation(base)]
+
+
+def device_parent(seed: int, n: int, k: int, group: int, device, std: float = 0.02,
+                  outlier_frac: float = 1e-3, outlier_mult: float = 10.0, c: int = C_BITS):
+    """The same recipe as `make_layer` + `minmax_parent`, drawn on `device` with
+    a seeded torch generator (for workloads too large to draw on the host):
+    W ~ N(0, std^2) fp32 with round(outlier_frac*n*k) entries x outlier_mult,
+    then per-group min-max quantization in fp32 (RNE), fp16 scale, integer zero.
+    Returns (q uint8 [n,k], scales fp16 [n,k/group], zeros fp16 [n,k/group])."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    w = torch.randn((n, k), generator=g, device=device, dtype=torch.float32) * std
+    n_out = int(round(outlier_frac * n * k))
+    if n_out:
+        idx = torch.randint(0, n * k, (n_out,), generator=g, device=device)
+        w.view(-1)[idx] *= outlier_mult
+    qmax = float(2 ** c - 1)
+    wg = w.view(n, k // group, group)
+    lo = torch.clamp(wg.amin(dim=-1), max=0.0)
+    hi = torch.clamp(wg.amax(dim=-1), min=0.0)
+    s16 = ((hi - lo) / qmax).to(torch.float16)
+    s16 = torch.where(s16 == 0, torch.ones_like(s16), s16)
+    sf = s16.float()
+    z = torch.clamp(torch.round(-lo / sf), 0, qmax)
+    q = torch.clamp(torch.round(wg / sf.unsqueeze(-1)) + z.unsqueeze(-1), 0, qmax)
+    del w, wg
+    return q.to(torch.uint8).view(n, k).contiguous(), s16.contiguous(), z.to(torch.float16).contiguous()
