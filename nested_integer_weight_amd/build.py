@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmq.so")
-SOURCES = ["mq_api.hip", "mq_pack.hip", "mq_gemv.hip", "mq_gemm.hip"]
+SOURCES = ["mq_api.hip", "mq_pack.hip", "mq_gemv.hip", "mq_gemm.hip", "mq_skinny.hip"]
 ARCH = os.environ.get("MQ_OFFLOAD_ARCH", "gfx950")
 
 COMMON = [

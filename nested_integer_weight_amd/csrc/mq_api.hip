@@ -88,6 +88,9 @@ mq_status run_linear(const void* x, int x_dtype, int m, const mq_packed* w, int 
   hipError_t e;
   if (gemv_eligible(m, w->k, a.bf16)) {
     e = launch_gemv(a, s);
+  } else if (skinny_eligible(m, w->k)) {
+    const bool ws_ok = workspace && aligned16(workspace);
+    e = launch_skinny(a, ws_ok ? workspace : nullptr, ws_ok ? workspace_bytes : 0, s);
   } else {
     GemmPlan plan = plan_gemm(m, w->n, w->k, workspace ? workspace_bytes : 0);
     if (plan.splits > 1 && !aligned16(workspace)) plan.splits = 1;
@@ -144,6 +147,9 @@ mq_status mq_pack_parent(const uint8_t* codes, int32_t n, int32_t k, const mq_pa
 size_t mq_linear_workspace_bytes(int32_t m, int32_t n, int32_t k) {
   if (check_shape(n, k) != MQ_OK || m <= 0) return 0;
   if (m <= kGemvMaxM && k <= kGemvMaxK && m == 1) return 0;
+  // the dtype is not known here: fp16 batches of up to 4 rows take the GEMV
+  // (no workspace), bf16 ones the skinny path, so size for the latter
+  if (skinny_eligible(m, k)) return skinny_workspace_bytes(m, n, k);
   return gemm_workspace_bytes(m, n, k);
 }
 

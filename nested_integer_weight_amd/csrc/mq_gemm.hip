@@ -1,4 +1,4 @@
-// mq_gemm.hip -- MFMA path for m > 4 (skinny decode batches and prefill).
+// mq_gemm.hip -- MFMA path for prefill and batches the skinny and GEMV paths do not take.
 //
 // Y[m, n] = sum_k X[m, k] * w_hat[n, k].  Per 64-wide k step a workgroup
 //  * copies its X tile (BM x 64, fp16/bf16) global -> VGPR -> LDS,
@@ -299,8 +299,22 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
                                                             uint16_t* __restrict__ y) {
   size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= mn) return;
+  // loads are issued eight at a time; the sum is still taken in split order
   float t = 0.f;
-  for (int s = 0; s < splits; ++s) t += ws[(size_t)s * mn + i];
+  int s = 0;
+  for (; s + 8 <= splits; s += 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = ws[(size_t)(s + j) * mn + i];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t += v[j];
+  }
+  float v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = s + j < splits ? ws[(size_t)(s + j) * mn + i] : 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (s + j < splits) t += v[j];
   y[i] = (uint16_t)((BF16 ? pack_bf16x2(t, 0.f) : pack_f16x2(t, 0.f)) & 0xFFFFu);
 }
 
@@ -424,14 +438,18 @@ hipError_t launch_gemm(const LinearArgs& la, const GemmPlan& plan, void* workspa
   }
 #undef MQ_GEMM_CASE
   if (e != hipSuccess || splits == 1) return e;
-  const size_t mn = (size_t)la.m * (size_t)la.n;
+  return launch_splitk_reduce(static_cast<const float*>(workspace), splits, (size_t)la.m * (size_t)la.n, la.y,
+                              la.bf16, s);
+}
+
+hipError_t launch_splitk_reduce(const float* ws, int splits, size_t mn, void* y, int bf16, hipStream_t s) {
   const unsigned blocks = (unsigned)((mn + 255) / 256);
-  if (la.bf16)
-    hipLaunchKernelGGL(splitk_reduce_kernel<1>, dim3(blocks), dim3(256), 0, s, static_cast<const float*>(workspace),
-                       splits, mn, static_cast<uint16_t*>(la.y));
+  if (bf16)
+    hipLaunchKernelGGL(splitk_reduce_kernel<1>, dim3(blocks), dim3(256), 0, s, ws, splits, mn,
+                       static_cast<uint16_t*>(y));
   else
-    hipLaunchKernelGGL(splitk_reduce_kernel<0>, dim3(blocks), dim3(256), 0, s, static_cast<const float*>(workspace),
-                       splits, mn, static_cast<uint16_t*>(la.y));
+    hipLaunchKernelGGL(splitk_reduce_kernel<0>, dim3(blocks), dim3(256), 0, s, ws, splits, mn,
+                       static_cast<uint16_t*>(y));
   return hipGetLastError();
 }
 

@@ -37,6 +37,21 @@ __host__ inline bool gemv_eligible(int m, int k, int bf16) {
 }
 hipError_t launch_gemv(const LinearArgs& a, hipStream_t s);
 
+// MFMA skinny path (weights dequantized straight into MFMA operand registers,
+// activations shared through LDS): 2 <= m <= 64 with k a multiple of 256.
+constexpr int kSkinnyMaxM = 64;
+__host__ inline bool skinny_eligible(int m, int k) { return m >= 2 && m <= kSkinnyMaxM && k % 256 == 0; }
+struct SkinnyPlan {
+  int splits;            // k ranges (1 = no workspace)
+  int rounds_per_split;  // 256-wide k rounds per range
+};
+SkinnyPlan plan_skinny(int m, int n, int k);
+size_t skinny_workspace_bytes(int m, int n, int k);
+hipError_t launch_skinny(const LinearArgs& a, void* workspace, size_t workspace_bytes, hipStream_t s);
+
+// fixed-order sum of fp32 split-k partials ws[splits][mn] rounded once into y (fp16 or bf16)
+hipError_t launch_splitk_reduce(const float* ws, int splits, size_t mn, void* y, int bf16, hipStream_t s);
+
 // MFMA GEMM (dequantized weight tiles in LDS), any m >= 1.
 struct GemmPlan {
   int cfg;       // tile configuration index

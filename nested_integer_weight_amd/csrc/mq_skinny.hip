@@ -1,0 +1,390 @@
+// mq_skinny.hip -- MFMA path for small decode batches (2 <= m <= 64).
+//
+// Y[m, n] = sum_k X[m, k] * w_hat[n, k] with the weights streamed straight from
+// the bit planes into MFMA operand registers: no LDS round trip and no
+// workgroup barrier for the weights, which are the HBM stream at these batch
+// sizes.  Only the activations (a few KB per round) go through LDS, because
+// every wave of a workgroup uses the same X slice.
+//
+// Work split.  A workgroup has 4 waves; wave w owns output rows
+// n0 + 32 w + 16 t + c (t = 0, 1; c = lane % 16).  The k range of a workgroup
+// is walked in rounds of 256: in a round, lane group g = lane / 16 owns the
+// 64 consecutive codes [64 g, 64 g + 64) of each of its two rows, i.e. one
+// 16-byte load per 2-bit plane and one 8-byte load per 1-bit plane.  MFMA
+// k-step i (0..7) of v_mfma_f32_16x16x32_{f16,bf16} takes from lane group g
+// the codes [64 g + 8 i, 64 g + 8 i + 8); the activation fragments in LDS
+// use the same k order, so every product pairs X[m, k] with w_hat[n, k].
+// A 64-code chunk never straddles a quantization group (group % 64 == 0),
+// so each lane needs one scale and zero point per row and round.
+//
+// Operand values.  The weight operand is w_hat = s * (v - z) (+ delta_r for
+// the true-prefix rule, MatGPTQ "Efficient and Accurate Inference over
+// Nested Quantized Models", section 3, reconstruction with the centring
+// offset) rounded once to the activation dtype:
+//   fp16: the byte v becomes the exact half 1024 + v (v_perm with an 0x64
+//         exponent byte); subtracting 1024 and adding (delta - z) are exact
+//         in half precision (|v - z + delta| <= 255.5 on a 0.5 grid), and the
+//         multiply by the fp16 scale rounds once to nearest even -- the same
+//         value as rounding the exact product.
+//   bf16: exact in fp32 (v * s + (delta - z) * s), then one RNE to bf16.
+// Accumulation is fp32 in the MFMA.
+//
+// Split-k: blockIdx.y picks a k range; with more than one range the fp32
+// partial tiles go to workspace[split][m][n] and the fixed-order reduction
+// kernel of the GEMM path sums them, so results stay deterministic.
+#include "mq_common.h"
+#include "mq_kernels.h"
+
+namespace mq {
+
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+// native vectors, not HIP's uint4/uint2 structs: copies of those go through
+// memcpy and would pin the staging registers in memory
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWaves = 4;
+constexpr int kNT = 2;                        // 16-row output tiles per wave
+constexpr int kColsPerBlock = 16 * kNT * kWaves;  // 128
+constexpr int kRound = 256;                   // k per round
+
+struct SkinnyArgs {
+  const uint16_t* x;
+  void* y;  // [m, n] in x's dtype, or fp32 workspace [splits][m][n]
+  PlanePtrs pl;
+  const uint16_t* scales;
+  const uint16_t* zeros;
+  int m, n, k, group;
+  int rounds_per_split;
+  int to_workspace;
+};
+
+template <int BF16>
+__device__ __forceinline__ f32x4 mfma(const u32x4& a, const u32x4& b, const f32x4& c) {
+  if constexpr (BF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                   0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0,
+                                                  0);
+  }
+}
+
+// RNE(s * (v - z + delta)) for two code bytes given as the halves 1024 + v
+__device__ __forceinline__ uint32_t dq_f16x2(uint32_t magic_pair, f16x2 c, f16x2 s) {
+  const f16x2 k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+  f16x2 v = __builtin_bit_cast(f16x2, magic_pair);
+  v = v - k1024;  // exact: the code value
+  v = v + c;      // exact: v - z + delta
+  v = v * s;      // the one rounding
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+template <int R, int ROUND, int BF16, int MT>
+struct SkinnyWave {
+  static constexpr int NP = planes_needed(R, ROUND);
+  static constexpr float kDelta = ROUND ? 0.0f : prefix_delta(R);
+  static constexpr int XPIECES = 2 * MT;  // 16-byte X pieces per thread per round
+
+  // weight slots in flight: rounds with few planes carry little data, so they
+  // are loaded two rounds ahead; wider ones one round ahead
+  static constexpr int kSlots = NP <= 3 ? 3 : 2;
+
+  const SkinnyArgs a;  // by value: a reference would make the compiler keep a copy in memory
+  int tid, lane, g, c, nw, kb0;
+  size_t upr;
+  int gpr;
+  // weights of one round per slot: [slot][tile][unit][word]
+  uint32_t rec[kSlots][kNT][2][kUnitWords];
+  // raw fp16 bits of scale and zero, zero-extended by the load itself (no
+  // arithmetic before use, so the loads stay in flight)
+  uint32_t sraw[kSlots][kNT], zraw[kSlots][kNT];
+  u32x4 xreg[XPIECES];
+  f32x4 acc[MT][kNT];
+
+  __device__ __forceinline__ SkinnyWave(const SkinnyArgs& args, int t, int n0, int kbase) : a(args), tid(t), kb0(kbase) {
+    lane = t & 63;
+    g = lane >> 4;
+    c = lane & 15;
+    nw = n0 + 32 * (t >> 6);
+    upr = (size_t)(a.k >> 5);
+    gpr = a.k / a.group;
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < kNT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // X piece p = tid + 256 j is lane p % 64 of LDS block p / 64 = (m tile, k step):
+  // row 16 (b / 8) + lane % 16, k 64 (lane / 16) + 8 (b % 8) of the round.
+  // Rows past m are clamped; they only feed output rows that are not stored.
+  __device__ __forceinline__ void load_x(int rnd) {
+    const int kr = kb0 + rnd * kRound;
+#pragma unroll
+    for (int j = 0; j < XPIECES; ++j) {
+      const int p = tid + 256 * j;
+      const int b = p >> 6, l = p & 63;
+      const int row = min(16 * (b >> 3) + (l & 15), a.m - 1);
+      const int col = kr + 64 * (l >> 4) + 8 * (b & 7);
+      xreg[j] = *reinterpret_cast<const u32x4*>(a.x + (size_t)row * a.k + col);
+    }
+  }
+  __device__ __forceinline__ void store_x(u32x4* xs) {
+#pragma unroll
+    for (int j = 0; j < XPIECES; ++j) xs[tid + 256 * j] = xreg[j];
+  }
+
+  // plane words, scale and zero of row tile T for the round starting at code kc
+  template <int SLOT, int T>
+  __device__ __forceinline__ void load_w_tile(int kc) {
+    const int row = min(nw + 16 * T + c, a.n - 1);
+    const size_t u0 = (size_t)row * upr + (size_t)(kc >> 5);  // even: k % 256 == 0
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      if (kPlaneBits[p] == 2) {
+        const u32x4 v = reinterpret_cast<const u32x4*>(a.pl.p[p])[u0 >> 1];
+        rec[SLOT][T][0][kUnitOff[p]] = v.x;
+        rec[SLOT][T][0][kUnitOff[p] + 1] = v.y;
+        rec[SLOT][T][1][kUnitOff[p]] = v.z;
+        rec[SLOT][T][1][kUnitOff[p] + 1] = v.w;
+      } else {
+        const u32x2 v = reinterpret_cast<const u32x2*>(a.pl.p[p])[u0 >> 1];
+        rec[SLOT][T][0][kUnitOff[p]] = v.x;
+        rec[SLOT][T][1][kUnitOff[p]] = v.y;
+      }
+    }
+    const size_t gi = (size_t)row * gpr + (size_t)(kc / a.group);
+    sraw[SLOT][T] = a.scales[gi];
+    zraw[SLOT][T] = a.zeros[gi];
+  }
+  template <int SLOT>
+  __device__ __forceinline__ void load_w(int rnd) {
+    const int kc = kb0 + rnd * kRound + 64 * g;  // first code of this lane's chunk
+    static_assert(kNT == 2, "two row tiles per wave");
+    load_w_tile<SLOT, 0>(kc);
+    load_w_tile<SLOT, 1>(kc);
+  }
+
+  // weight operand of MFMA k-step I for row tile T: codes [8 I, 8 I + 8) of the chunk
+  // (every array index here is a compile-time constant, so the staging arrays
+  // stay in registers)
+  template <int SLOT, int I, int T>
+  __device__ __forceinline__ u32x4 w_frag() const {
+    const uint32_t* u = rec[SLOT][T][I >> 2];
+    constexpr int J0 = 2 * (I & 3);
+    const uint32_t w0 = slice_bytes<R, ROUND>(assemble_word<NP, J0>(u));
+    const uint32_t w1 = slice_bytes<R, ROUND>(assemble_word<NP, J0 + 1>(u));
+    if constexpr (BF16) {
+      const float s = h2f((uint16_t)sraw[SLOT][T]);
+      const float cz = (kDelta - h2f((uint16_t)zraw[SLOT][T])) * s;  // exact
+      u32x4 f;
+      f.x = pack_bf16x2(fmaf((float)(w0 & 0xFFu), s, cz), fmaf((float)((w0 >> 8) & 0xFFu), s, cz));
+      f.y = pack_bf16x2(fmaf((float)((w0 >> 16) & 0xFFu), s, cz), fmaf((float)(w0 >> 24), s, cz));
+      f.z = pack_bf16x2(fmaf((float)(w1 & 0xFFu), s, cz), fmaf((float)((w1 >> 8) & 0xFFu), s, cz));
+      f.w = pack_bf16x2(fmaf((float)((w1 >> 16) & 0xFFu), s, cz), fmaf((float)(w1 >> 24), s, cz));
+      return f;
+    } else {
+      const _Float16 sh = __builtin_bit_cast(_Float16, (uint16_t)sraw[SLOT][T]);
+      const _Float16 ch = (_Float16)(kDelta - h2f((uint16_t)zraw[SLOT][T]));  // exact: |delta - z| <= 255.5
+      const f16x2 s2 = {sh, sh};
+      const f16x2 c2 = {ch, ch};
+      u32x4 f;
+      f.x = dq_f16x2(__builtin_amdgcn_perm(0x64646464u, w0, 0x04010400u), c2, s2);
+      f.y = dq_f16x2(__builtin_amdgcn_perm(0x64646464u, w0, 0x04030402u), c2, s2);
+      f.z = dq_f16x2(__builtin_amdgcn_perm(0x64646464u, w1, 0x04010400u), c2, s2);
+      f.w = dq_f16x2(__builtin_amdgcn_perm(0x64646464u, w1, 0x04030402u), c2, s2);
+      return f;
+    }
+  }
+
+  template <int SLOT, int I>
+  __device__ __forceinline__ void kstep(const u32x4* xs) {
+    const u32x4 wf0 = w_frag<SLOT, I, 0>();
+    const u32x4 wf1 = w_frag<SLOT, I, 1>();
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const u32x4 xf = xs[(mt * 8 + I) * 64 + lane];
+      acc[mt][0] = mfma<BF16>(xf, wf0, acc[mt][0]);
+      acc[mt][1] = mfma<BF16>(xf, wf1, acc[mt][1]);
+    }
+  }
+
+  template <int SLOT>
+  __device__ __forceinline__ void compute(const u32x4* xs) {
+    kstep<SLOT, 0>(xs);
+    kstep<SLOT, 1>(xs);
+    kstep<SLOT, 2>(xs);
+    kstep<SLOT, 3>(xs);
+    kstep<SLOT, 4>(xs);
+    kstep<SLOT, 5>(xs);
+    kstep<SLOT, 6>(xs);
+    kstep<SLOT, 7>(xs);
+  }
+
+  // Round rnd computes from slot SLOT and LDS buffer rnd & 1.  It first issues
+  // the X loads of round rnd + 1 and then the weight loads of round
+  // rnd + kSlots - 1 (into the slot of round rnd - 1), in that order, so that
+  // staging X at the end of the round waits for the X loads only and the
+  // weights stay in flight across the barrier.  Past the last round the loads
+  // repeat it.
+  template <int SLOT>
+  __device__ __forceinline__ void round(int rnd, int last, u32x4* xs0, u32x4* xs1) {
+    load_x(min(rnd + 1, last));
+    __builtin_amdgcn_sched_barrier(0);
+    load_w<(SLOT + kSlots - 1) % kSlots>(min(rnd + kSlots - 1, last));
+    compute<SLOT>((rnd & 1) ? xs1 : xs0);
+    store_x((rnd & 1) ? xs0 : xs1);
+    __syncthreads();
+  }
+
+  __device__ __forceinline__ void run(int nr, u32x4* xs0, u32x4* xs1) {
+    const int last = nr - 1;
+    load_x(0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_w<0>(0);
+    if constexpr (kSlots == 3) load_w<1>(min(1, last));
+    store_x(xs0);
+    __syncthreads();
+    int r = 0;
+    if constexpr (kSlots == 3) {
+      for (; r + 2 < nr; r += 3) {
+        round<0>(r, last, xs0, xs1);
+        round<1>(r + 1, last, xs0, xs1);
+        round<2>(r + 2, last, xs0, xs1);
+      }
+      if (r < nr) round<0>(r, last, xs0, xs1);
+      if (r + 1 < nr) round<1>(r + 1, last, xs0, xs1);
+    } else {
+      for (; r + 1 < nr; r += 2) {
+        round<0>(r, last, xs0, xs1);
+        round<1>(r + 1, last, xs0, xs1);
+      }
+      if (r < nr) round<0>(r, last, xs0, xs1);
+    }
+  }
+};
+
+// Two waves per SIMD is enough to cover the latency with the prefetch above;
+// asking for more would make the compiler spill the staging registers.
+template <int R, int ROUND, int BF16, int MT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void skinny_kernel(SkinnyArgs a) {
+  __shared__ u32x4 Xs0[MT * 8 * 64];
+  __shared__ u32x4 Xs1[MT * 8 * 64];
+  const int tid = threadIdx.x;
+  const int n0 = blockIdx.x * kColsPerBlock;
+  const int kb0 = blockIdx.y * a.rounds_per_split * kRound;
+  const int nr = min(a.rounds_per_split, (a.k - kb0) / kRound);
+  SkinnyWave<R, ROUND, BF16, MT> w(a, tid, n0, kb0);
+  if (nr > 0) w.run(nr, Xs0, Xs1);
+  // lane holds D[4 (lane / 16) + v][lane % 16] of every (m tile, row tile)
+  const int lane = tid & 63;
+  const int nb = n0 + 32 * (tid >> 6) + (lane & 15);
+  const int mb = 4 * (lane >> 4);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int t = 0; t < kNT; ++t) {
+      const int nn = nb + 16 * t;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int mm = 16 * mt + mb + v;
+        if (mm < a.m && nn < a.n) {
+          const float val = w.acc[mt][t][v];
+          if (a.to_workspace) {
+            static_cast<float*>(a.y)[((size_t)blockIdx.y * a.m + mm) * a.n + nn] = val;
+          } else {
+            uint16_t* y = static_cast<uint16_t*>(a.y) + (size_t)mm * a.n + nn;
+            *y = (uint16_t)((BF16 ? pack_bf16x2(val, 0.f) : pack_f16x2(val, 0.f)) & 0xFFFFu);
+          }
+        }
+      }
+    }
+  }
+}
+
+constexpr int kTargetBlocks = 448;  // 1.75 workgroups per CU
+
+int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
+
+template <int R, int ROUND, int BF16>
+hipError_t launch_t(const SkinnyArgs& sa, int mt, dim3 grid, hipStream_t s) {
+  switch (mt) {
+    case 1: hipLaunchKernelGGL((skinny_kernel<R, ROUND, BF16, 1>), grid, dim3(256), 0, s, sa); break;
+    case 2: hipLaunchKernelGGL((skinny_kernel<R, ROUND, BF16, 2>), grid, dim3(256), 0, s, sa); break;
+    case 3: hipLaunchKernelGGL((skinny_kernel<R, ROUND, BF16, 3>), grid, dim3(256), 0, s, sa); break;
+    default: hipLaunchKernelGGL((skinny_kernel<R, ROUND, BF16, 4>), grid, dim3(256), 0, s, sa); break;
+  }
+  return hipGetLastError();
+}
+
+template <int R, int ROUND>
+hipError_t launch_d(const SkinnyArgs& sa, int bf16, int mt, dim3 grid, hipStream_t s) {
+  return bf16 ? launch_t<R, ROUND, 1>(sa, mt, grid, s) : launch_t<R, ROUND, 0>(sa, mt, grid, s);
+}
+
+}  // namespace
+
+SkinnyPlan plan_skinny(int m, int n, int k) {
+  SkinnyPlan p;
+  const int rounds = k / kRound;
+  const int blocks_n = cdiv(n, kColsPerBlock);
+  int s = cdiv(kTargetBlocks, blocks_n);
+  if (s > rounds) s = rounds;
+  if (s < 1) s = 1;
+  p.rounds_per_split = cdiv(rounds, s);
+  p.splits = cdiv(rounds, p.rounds_per_split);
+  (void)m;
+  return p;
+}
+
+size_t skinny_workspace_bytes(int m, int n, int k) {
+  if (!skinny_eligible(m, k)) return 0;
+  const SkinnyPlan p = plan_skinny(m, n, k);
+  return p.splits > 1 ? (size_t)p.splits * (size_t)m * (size_t)n * sizeof(float) : 0;
+}
+
+hipError_t launch_skinny(const LinearArgs& la, void* workspace, size_t workspace_bytes, hipStream_t s) {
+  SkinnyPlan p = plan_skinny(la.m, la.n, la.k);
+  if (p.splits > 1 && workspace_bytes < (size_t)p.splits * (size_t)la.m * (size_t)la.n * sizeof(float)) {
+    p.splits = 1;
+    p.rounds_per_split = la.k / kRound;
+  }
+  SkinnyArgs sa;
+  sa.x = static_cast<const uint16_t*>(la.x);
+  sa.pl = la.pl;
+  sa.scales = la.scales;
+  sa.zeros = la.zeros;
+  sa.m = la.m;
+  sa.n = la.n;
+  sa.k = la.k;
+  sa.group = la.group;
+  sa.rounds_per_split = p.rounds_per_split;
+  sa.to_workspace = p.splits > 1;
+  sa.y = p.splits > 1 ? workspace : la.y;
+  const int mt = cdiv(la.m, 16);
+  const dim3 grid((unsigned)cdiv(la.n, kColsPerBlock), (unsigned)p.splits);
+  hipError_t e;
+#define MQ_SK_CASE(RR)                                                                               \
+  case RR:                                                                                           \
+    e = la.round_rule ? launch_d<RR, 1>(sa, la.bf16, mt, grid, s) : launch_d<RR, 0>(sa, la.bf16, mt, grid, s); \
+    break;
+  switch (la.r) {
+    MQ_SK_CASE(2)
+    MQ_SK_CASE(3)
+    MQ_SK_CASE(4)
+    MQ_SK_CASE(6)
+    MQ_SK_CASE(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef MQ_SK_CASE
+  if (e != hipSuccess || p.splits == 1) return e;
+  return launch_splitk_reduce(static_cast<const float*>(workspace), p.splits, (size_t)la.m * (size_t)la.n, la.y,
+                              la.bf16, s);
+}
+
+}  // namespace mq

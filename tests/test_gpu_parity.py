@@ -124,6 +124,11 @@ SHAPES = [
     (8, 257, 1024, 64, "f16"),
     (17, 129, 2048, 128, "bf16"),
     (63, 64, 512, 64, "f16"),
+    (4, 70, 768, 64, "bf16"),       # skinny MFMA path: bf16 m = 4, three k rounds
+    (16, 1, 256, 64, "f16"),        # skinny: a single output column and round
+    (33, 200, 1536, 256, "f16"),    # skinny: three m tiles, group 256
+    (49, 130, 2304, 128, "bf16"),   # skinny: four m tiles, nine rounds split nine ways
+    (64, 17, 4352, 128, "f16"),     # skinny: seventeen rounds, ragged n
     (65, 300, 768, 64, "bf16"),
     (257, 300, 512, 128, "bf16"),
     (300, 520, 1024, 128, "f16"),
