@@ -13,11 +13,15 @@ weight reads come from HBM, not the last-level cache.
 
 Printed JSON (one line): value = algorithmic bytes of all calls / wall time of
 the timed steps (GB/s).  Algorithmic bytes per call = bit planes the width
-reads + 4 B (fp16 scale + zero) per group + X (2*M*K) + Y (2*M*N).
-`roofline` is for the kernel that takes the most time per step (the r = 8
-decode GEMV): its bytes per launch over its average launch duration, measured
-with HIP events on the launch stream during the timed steps.  `per_r` gives
-the same figure for every width.  `prefill` times the M = 2048 bf16 prefill
+reads + 4 B (fp16 scale + zero) per group + X (2*M*K) + Y (2*M*N).  The timed
+steps are replayed from HIP graphs that each hold `ring` consecutive steps in
+the eager order (checked bit for bit against the eager calls before timing),
+which is how a serving loop issues them; `eager` reports the same steps issued
+as one C-ABI call per width, host launch gaps included.  `roofline` is for the
+kernel that takes the most time per step (the r = 8 decode GEMV): its bytes
+per launch over its average launch duration, from HIP events on the launch
+stream around replays of a graph of r = 8 calls only.  `per_r` gives the same
+figure for every width.  `prefill` times the M = 2048 bf16 prefill
 GEMM (same shapes, r in {2, 4, 8}) against the dense bf16 MFMA peak.
 `skinny` times decode batches M in {8, 16, 32, 64} at r in {2, 3, 4, 8} on the
 same shapes against max(HBM time, MFMA time).  `mixnmatch` times one pass over
@@ -73,6 +77,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--ring", type=int, default=8, help="distinct parent copies cycled through")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--eager", action="store_true", help="time eager calls only (no HIP graph replay)")
     ap.add_argument("--cpu-steps", type=int, default=3, help="workload steps the CPU oracle baseline times")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill GEMM lines")
     ap.add_argument("--prefill-iters", type=int, default=10)
@@ -136,36 +141,115 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} steps done")
 
-    # ---------------- timed steps ----------------
-    ev = {r: [] for r in WIDTHS}
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for i in range(args.steps):
-        step = args.warmup + i
-        for r in WIDTHS:
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            mq.linear_mixed(calls_for(step, r))
-            e1.record(stream)
-            ev[r].append((e0, e1))
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms_per_step = total_ms / args.steps
-    value = bytes_step * args.steps / (total_ms * 1e-3) / 1e9
-    log(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step, {value:.1f} GB/s")
+    # ---------------- eager timed steps (one C-ABI call per width and step) ----------------
+    def eager_run(n_steps, first):
+        ev = {r: [] for r in WIDTHS}
+        t0_, t1_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0_.record(stream)
+        for i in range(n_steps):
+            for r in WIDTHS:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                mq.linear_mixed(calls_for(first + i, r))
+                e1.record(stream)
+                ev[r].append((e0, e1))
+        t1_.record(stream)
+        torch.cuda.synchronize()
+        return t0_.elapsed_time(t1_), ev
 
-    per_r = {}
-    for r in WIDTHS:
-        ms = float(np.mean([a.elapsed_time(b) for a, b in ev[r]]))
-        per_launch_us = ms * 1e3 / len(mats)
-        b_launch = bytes_r[r] / len(mats)
-        gbs = b_launch / (per_launch_us * 1e-6) / 1e9
-        per_r[str(r)] = {"us_per_launch": round(per_launch_us, 3), "bytes_per_launch": int(b_launch),
-                         "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+    eager_ms, ev = eager_run(args.steps, args.warmup)
+    eager = {"value": round(bytes_step * args.steps / (eager_ms * 1e-3) / 1e9, 1),
+             "ms_per_step": round(eager_ms / args.steps, 5)}
+    log(f"[bench] eager {args.steps} steps: {eager['ms_per_step'] * 1e3:.1f} us/step, {eager['value']} GB/s")
+
+    def per_r_from(ms_of_r, launches):
+        out = {}
+        for r in WIDTHS:
+            per_launch_us = ms_of_r[r] * 1e3 / launches
+            b_launch = bytes_r[r] / len(mats)
+            gbs = b_launch / (per_launch_us * 1e-6) / 1e9
+            out[str(r)] = {"us_per_launch": round(per_launch_us, 3), "bytes_per_launch": int(b_launch),
+                           "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+        return out
+
+    # ---------------- HIP graph replay (the serving form of the step) ----------------
+    # One graph holds `ring` consecutive steps in the eager order of widths and
+    # parent copies, so each replay still reads every weight byte from HBM; the
+    # host issues one launch per `ring` steps instead of one call per width.
+    mode = "eager"
+    per_r = per_r_from({r: float(np.mean([a.elapsed_time(b) for a, b in ev[r]])) for r in WIDTHS}, len(mats))
+    value, ms_per_step, timed_steps = eager["value"], eager["ms_per_step"], args.steps
+    if not args.eager:
+        ring = args.ring
+        # eager reference of the last step of the ring, then the graph's last step must match it
+        for r in WIDTHS:
+            mq.linear_mixed(calls_for(ring - 1, r))
+        torch.cuda.synchronize()
+        ref = [mt["y"].clone() for mt in mats]
+        g_step = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_step):
+            for i in range(ring):
+                for r in WIDTHS:
+                    mq.linear_mixed(calls_for(i, r))
+        rem = args.steps % ring  # leftover steps, so that exactly --steps steps are timed
+        g_rem = None
+        if rem:
+            g_rem = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g_rem):
+                for i in range(rem):
+                    for r in WIDTHS:
+                        mq.linear_mixed(calls_for(i, r))
+        g_r = {}
+        for r in WIDTHS:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(ring):
+                    mq.linear_mixed(calls_for(i, r))
+            g_r[r] = g
+        ok = True
+        for rep in range(2):  # replays interleaved with eager work and synchronisation
+            for mt in mats:
+                mt["y"].zero_()
+            g_step.replay()
+            torch.cuda.synchronize()
+            ok = ok and all(torch.equal(mt["y"], y0) for mt, y0 in zip(mats, ref))
+            mq.linear_mixed(calls_for(0, 2))
+            torch.cuda.synchronize()
+        if not ok:
+            log("[bench] graph replay differs from the eager step: reporting eager timing")
+        else:
+            reps = args.steps // ring
+            timed_steps = args.steps
+            t0_, t1_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            t0_.record(stream)
+            for _ in range(reps):
+                g_step.replay()
+            if g_rem is not None:
+                g_rem.replay()
+            t1_.record(stream)
+            torch.cuda.synchronize()
+            g_ms = t0_.elapsed_time(t1_)
+            ms_per_step = g_ms / timed_steps
+            value = bytes_step * timed_steps / (g_ms * 1e-3) / 1e9
+            ms_r = {}
+            for r in WIDTHS:
+                g_r[r].replay()
+                torch.cuda.synchronize()
+                a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                reps_r = max(1, reps)
+                a_.record(stream)
+                for _ in range(reps_r):
+                    g_r[r].replay()
+                b_.record(stream)
+                torch.cuda.synchronize()
+                ms_r[r] = a_.elapsed_time(b_) / reps_r / ring
+            per_r = per_r_from(ms_r, len(mats))
+            mode = "hip_graph"
+            log(f"[bench] graph {timed_steps} steps: {ms_per_step * 1e3:.1f} us/step, {value:.1f} GB/s")
+        del g_step, g_r, g_rem
     dom = per_r["8"]
 
     traffic = None
@@ -325,13 +409,15 @@ def main():
         log(f"[bench] cpu oracle: {cpu['value']} GB/s in {dt:.1f}s")
 
     out = {
-        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": timed_steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
         "config": {"workload": "llama3.1-8b-ffn decode: gate/up 4096->14336 + down 14336->4096, M=1, "
                                "g=128, true-prefix, r in {2,3,4,6,8}",
                    "global_batch": 1, "widths": list(WIDTHS), "ring_copies": args.ring},
         "roofline": roofline,
+        "timing": mode,
+        "eager": eager,
         "per_r": per_r,
         "prefill": prefill,
         "skinny": skinny,

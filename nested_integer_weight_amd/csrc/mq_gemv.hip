@@ -107,9 +107,11 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   // width 2, true prefix, fp16: fields go straight from the plane-0 word to
   // fp16 with one and-or per pair (no byte assembly)
   constexpr bool FAST2 = (R == 2 && !ROUND && !BF16);
-  // rows per load batch: batch b + 1 is in flight while batch b is computed;
-  // small batches shorten the compute tail after the last bytes arrive
-  constexpr int RB = 2;
+  // rows per load batch: batch b + 1 is in flight while batch b is computed.
+  // Narrow widths carry few bytes per row, so all rows of the block are
+  // requested at once to keep enough bytes in flight; wide ones use small
+  // batches, which shortens the compute tail after the last bytes arrive.
+  constexpr int RB = NP <= 3 ? ROWS : 2;
   constexpr int NB = ROWS / RB;
   static_assert(NB * RB == ROWS, "row batches");
   constexpr int V = ROWS * MT;

@@ -239,3 +239,31 @@ def test_gemma_mixnmatch_blocks(mq, m, dt):
     outs = mq.linear_mixed(calls)
     for (lay, x, r), y in zip(meta, outs):
         check_y(y, lay, x, r, O.PREFIX, rows=sample_rows(lay.n, 16))
+
+
+def test_graph_replay_matches_eager(mq):
+    # the serving form: calls captured in a HIP graph (GEMV, skinny with split-k,
+    # GEMM with split-k) replay bit for bit like the eager calls, replay after
+    # replay, with eager work and synchronisation in between
+    calls = []
+    for i, (r, m, dt, n, k) in enumerate([(2, 1, "f16", 512, 4096), (4, 16, "f16", 640, 4096),
+                                          (8, 40, "bf16", 384, 2048), (3, 300, "bf16", 520, 1024)]):
+        lay = synth.make_layer(cfg_id=7, tensor_id=i, n=n, k=k, m=m, group=128, x_dtype=dt)
+        q, s, z = to_dev(lay)
+        x = lay.x.to(DEV)
+        calls.append(mq.Call(x=x, packed=mq.pack_parent(q), r=r, rule=O.PREFIX, group=128, scales=s, zeros=z,
+                             out=torch.empty((m, n), dtype=x.dtype, device=DEV)))
+    eager = [y.clone() for y in mq.linear_mixed(calls)]
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mq.linear_mixed(calls)
+    for rep in range(3):
+        for c in calls:
+            c.out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for c, y0 in zip(calls, eager):
+            assert torch.equal(c.out, y0), f"replay {rep} differs"
+        mq.linear_mixed(calls[:1])  # eager work between replays
+        torch.cuda.synchronize()
