@@ -27,7 +27,8 @@ GEMM (same shapes, r in {2, 4, 8}) against the dense bf16 MFMA peak.
 same shapes against max(HBM time, MFMA time).  `mixnmatch` times one pass over
 42 Gemma-2-9B FFN blocks (gate/up 3584->14336, down 14336->3584, g = 128) with
 the seeded per-block widths (14 each of 2, 3 and 4 bits) at M = 1 (fp16) and
-M = 256 (bf16); those parents are drawn on the device (same recipe).
+M = 256 (bf16), replayed from one HIP graph per pass (eager figure kept); those
+parents are drawn on the device (same recipe).
 `cpu_baseline` times the CPU oracle on all three matrices at every width.
 """
 from __future__ import annotations
@@ -363,16 +364,40 @@ def main():
             b_.record(stream)
             torch.cuda.synchronize()
             us = a_.elapsed_time(b_) * 1e3 / passes
+            eager_us = us
+            mode_mix = "eager"
+            if not args.eager:
+                # the same pass replayed from one HIP graph (checked bit for bit first)
+                ref = {nn: yy.clone() for nn, yy in yn.items()}
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    mq.linear_mixed(calls)
+                for yy in yn.values():
+                    yy.zero_()
+                g.replay()
+                torch.cuda.synchronize()
+                if all(torch.equal(yn[nn], ref[nn]) for nn in yn):
+                    a_.record(stream)
+                    for _ in range(passes):
+                        g.replay()
+                    b_.record(stream)
+                    torch.cuda.synchronize()
+                    us = a_.elapsed_time(b_) * 1e3 / passes
+                    mode_mix = "hip_graph"
+                else:
+                    log("[bench] mixnmatch graph replay differs from the eager pass: reporting eager timing")
+                del g
             byt = sum(alg_bytes(m, n, k, r) for (blk, name, n, k, r, pk, s_, z_) in blocks)
             fl = 2.0 * m * sum(n * k for (blk, name, n, k, r, pk, s_, z_) in blocks)
             if m == 1:
                 mix["m1"] = {"us_per_pass": round(us, 1), "GB/s": round(byt / (us * 1e-6) / 1e9, 1),
-                             "frac_hbm": round(byt / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "bytes": int(byt)}
+                             "frac_hbm": round(byt / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "bytes": int(byt),
+                             "timing": mode_mix, "eager_us_per_pass": round(eager_us, 1)}
             else:
                 mix["m256"] = {"us_per_pass": round(us, 1), "TFLOP/s": round(fl / (us * 1e-6) / 1e12, 1),
                                "frac_mfma_bf16": round(fl / (us * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
-                               "flop": fl}
-            log(f"[bench] mixnmatch m={m}: {us:.1f} us per pass of {len(blocks)} calls")
+                               "flop": fl, "timing": mode_mix, "eager_us_per_pass": round(eager_us, 1)}
+            log(f"[bench] mixnmatch m={m}: {us:.1f} us per pass of {len(blocks)} calls ({mode_mix}; eager {eager_us:.1f})")
         del blocks, calls
 
     if args.copy_calib_mib > 0:
