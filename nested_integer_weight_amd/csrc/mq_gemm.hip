@@ -349,16 +349,34 @@ static int pick_cfg(int m, int n) {
   return 0;  // 256 x 256: half the dequantization per MAC of a 128-row tile
 }
 
-// Split k so that tiles x splits fills the CUs (at most 16 splits, at least 8
-// k steps each); 1 when the tiles alone fill the GPU.
+// workgroups of a configuration that fit one CU's LDS (double-buffered X and W tiles)
+static int blocks_per_cu(int cfg) {
+  const int lds = 2 * (kCfgs[cfg].bm + kCfgs[cfg].bn) * BK * 2;
+  const int b = (160 * 1024) / lds;
+  return b < 1 ? 1 : (b > 2 ? 2 : b);
+}
+
+// When the tiles alone do not fill the GPU, split k to minimise (rounds of
+// workgroups over the CUs) x (k steps per split):
+// at most 16 splits of at least 8 k steps each; ties go to fewer splits, since
+// every split adds workspace traffic and a reduction.  So a split count whose
+// workgroups spill into a second, mostly idle round loses to a smaller one
+// that fits in a single round.
 static int pick_splits(int cfg, int m, int n, int k) {
   const int tiles = tiles_of(cfg, m, n);
   const int KT = k / BK;
-  if (tiles * 8 >= kCUs * 7) return 1;
-  int s = cdiv(kCUs, tiles);
-  if (s > kMaxSplits) s = kMaxSplits;
-  while (s > 1 && KT / s < 8) --s;
-  return s < 1 ? 1 : s;
+  if (tiles * 8 >= kCUs * 7) return 1;  // the tiles alone fill the GPU
+  const int slots = kCUs * blocks_per_cu(cfg);
+  int best_s = 1;
+  long best = (long)cdiv(tiles, slots) * KT;
+  for (int s = 2; s <= kMaxSplits && KT / s >= 8; ++s) {
+    const long t = (long)cdiv((long)tiles * s, slots) * cdiv(KT, s);
+    if (t < best) {
+      best = t;
+      best_s = s;
+    }
+  }
+  return best_s;
 }
 
 size_t gemm_workspace_bytes(int m, int n, int k) {
