@@ -131,6 +131,8 @@ SHAPES = [
     (64, 17, 4352, 128, "f16"),     # skinny: seventeen rounds, ragged n
     (65, 300, 768, 64, "bf16"),
     (257, 300, 512, 128, "bf16"),
+    (300, 448, 1024, 128, "bf16"),  # prefill tile with split k
+    (257, 672, 2048, 64, "f16"),    # prefill tile, ragged m, group 64
     (300, 520, 1024, 128, "f16"),
 ]
 
