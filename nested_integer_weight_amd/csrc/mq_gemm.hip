@@ -35,10 +35,13 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int BK = 64;
-// LDS tiles are fragment-major: a 16-row x 32-k block is 1 KB and lane l of
-// an MFMA operand read owns bytes [16 l, 16 l + 16) of it (row 16b + l % 16,
-// k 8 (l / 16) .. + 7 of the block's k half).  Every fragment read and every
-// staging write is a contiguous 1 KB per wave: no bank conflicts, no padding.
+// The weight tile in LDS is fragment-major: a 16-row x 32-k block is 1 KB and
+// lane l of an MFMA operand read owns 16 bytes of it (row 16b + l % 16, k
+// 8 (l / 16) .. + 7 of the block's k half), so every fragment read is one
+// contiguous 1 KB per wave.  The X tile is row-major with an xor swizzle
+// instead (see store_x), which lets its global loads take a whole row's k
+// slice per eight lanes.  ds_write_b128 serves eight consecutive lanes per
+// clock on gfx950, so the swizzles keep each such group on distinct banks.
 
 struct GemmArgs {
   const void* x;
@@ -96,27 +99,30 @@ struct GemmTile {
       for (int j = 0; j < FN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // X chunk c (16 B) is lane c % 64 of block c / 64 = (row16, k half):
-  // row 16 (c / 128) + c % 16, k 32 ((c / 64) % 2) + 8 ((c / 16) % 4).
-  // Unconditional loads from clamped addresses: X rows past m only feed
-  // output rows that are never stored.
+  // X chunk c (16 B) is row c / 8, k 8 (c % 8) .. + 7: eight consecutive lanes
+  // read one row's 128-byte k slice, so the vector cache sees one request per
+  // row instead of one per lane.  Unconditional loads from clamped addresses:
+  // X rows past m only feed output rows that are never stored.
   __device__ __forceinline__ void load_x(int kt) {
     const int k0 = kt * BK;
     const uint16_t* xg = static_cast<const uint16_t*>(a.x);
 #pragma unroll
     for (int i = 0; i < CX; ++i) {
       const int c = (tid + i * T) % (BM * 8);
-      const int row = 16 * (c >> 7) + (c & 15);
-      const int col = 32 * ((c >> 6) & 1) + 8 * ((c >> 4) & 3);
+      const int row = c >> 3, col = 8 * (c & 7);
       const int mrow = min(m0 + row, a.m - 1);
       xreg[i] = *reinterpret_cast<const uint4*>(xg + (size_t)mrow * a.k + k0 + col);
     }
   }
+  // the X tile in LDS is row-major, eight 16-byte chunks per row, with chunk
+  // c of row r stored at position c ^ (r % 8): the staging writes (eight
+  // lanes per row) and the MFMA fragment reads (sixteen rows, one chunk
+  // each) then both spread over all banks
   __device__ __forceinline__ void store_x(uint4* as) {
 #pragma unroll
     for (int i = 0; i < CX; ++i) {
       const int c = tid + i * T;
-      if ((BM * 8) % T == 0 || c < BM * 8) as[c] = xreg[i];
+      if ((BM * 8) % T == 0 || c < BM * 8) as[(c >> 3) * 8 + ((c & 7) ^ ((c >> 3) & 7))] = xreg[i];
     }
   }
   // weight item it -> (row it / 2, unit it % 2): a lane pair reads one row's two
@@ -177,22 +183,24 @@ struct GemmTile {
         h[2 * j + 1] = BF16 ? pack_bf16x2(w2, w3) : pack_f16x2(w2, w3);
       }
       // 8-k chunk j of this row's k half u is lane (row % 16) + 16 j of block (row / 16, u)
-      uint4* dst = bs + ((row >> 4) * 2 + u) * 64 + (row & 15);
+      // (positions in the second k half are xor-ed with 4 so that the lane
+      // pair of a row writes to different banks)
+      uint4* dst = bs + ((row >> 4) * 2 + u) * 64 + ((row & 15) ^ (4 * u));
       dst[0] = make_uint4(h[0], h[1], h[2], h[3]);
       dst[16] = make_uint4(h[4], h[5], h[6], h[7]);
       dst[32] = make_uint4(h[8], h[9], h[10], h[11]);
       dst[48] = make_uint4(h[12], h[13], h[14], h[15]);
     }
   }
-  // MFMAs of one 32-wide k half from LDS tiles as[BM/16][2][64], bs[BN/16][2][64]
+  // MFMAs of one 32-wide k half from LDS tiles as[BM][8], bs[BN/16][2][64]
   __device__ __forceinline__ void mma_half(const uint4* as, const uint4* bs, int kh, int lane, int wm, int wn) {
     {
       uint4 bfr[FN];
 #pragma unroll
-      for (int j = 0; j < FN; ++j) bfr[j] = bs[((wn * FN + j) * 2 + kh) * 64 + lane];
+      for (int j = 0; j < FN; ++j) bfr[j] = bs[((wn * FN + j) * 2 + kh) * 64 + (lane ^ (4 * kh))];
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        const uint4 af = as[((wm * FM + i) * 2 + kh) * 64 + lane];
+        const uint4 af = as[((wm * FM + i) * 16 + (lane & 15)) * 8 + ((kh * 4 + (lane >> 4)) ^ (lane & 7))];
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = mfma16x16x32<BF16>(af, bfr[j], acc[i][j]);
       }
@@ -204,8 +212,8 @@ template <int R, int ROUND, int BF16, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs a) {
   using Tile = GemmTile<R, ROUND, BF16, BM, BN, WM, WN>;
   constexpr int FM = Tile::FM, FN = Tile::FN;
-  // fragment-major LDS tiles, double buffered
-  __shared__ uint4 As[2][BM / 16 * 2 * 64];
+  // double-buffered LDS tiles: X swizzled row-major, weights fragment-major
+  __shared__ uint4 As[2][BM * 8];
   __shared__ uint4 Bs[2][BN / 16 * 2 * 64];
 
   const int tid = threadIdx.x;
