@@ -120,23 +120,30 @@ struct SkinnyWave {
       for (int j = 0; j < kNT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // X piece p = tid + 256 j is lane p % 64 of LDS block p / 64 = (m tile, k step):
-  // row 16 (b / 8) + lane % 16, k 64 (lane / 16) + 8 (b % 8) of the round.
+  // X piece p = tid + 256 j is 16-byte chunk q = p % 32 of row p / 32 of the
+  // round: 32 consecutive lanes read one row's 512 contiguous bytes.  The
+  // chunk holds k = 8 q .. 8 q + 7, i.e. k-step q % 8 of lane group q / 8, so
+  // it goes to LDS block (m tile, k step) = (row / 16, q % 8) at fragment
+  // position 16 (q / 8) + row % 16, xor-ed with the k step: the eight
+  // consecutive lanes that one ds_write_b128 clock serves then hit distinct
+  // banks, and the fragment reads (lane ^ step) stay contiguous per 8 lanes.
   // Rows past m are clamped; they only feed output rows that are not stored.
   __device__ __forceinline__ void load_x(int rnd) {
     const int kr = kb0 + rnd * kRound;
 #pragma unroll
     for (int j = 0; j < XPIECES; ++j) {
       const int p = tid + 256 * j;
-      const int b = p >> 6, l = p & 63;
-      const int row = min(16 * (b >> 3) + (l & 15), a.m - 1);
-      const int col = kr + 64 * (l >> 4) + 8 * (b & 7);
-      xreg[j] = *reinterpret_cast<const u32x4*>(a.x + (size_t)row * a.k + col);
+      const int row = min(p >> 5, a.m - 1);
+      xreg[j] = *reinterpret_cast<const u32x4*>(a.x + (size_t)row * a.k + kr + 8 * (p & 31));
     }
   }
   __device__ __forceinline__ void store_x(u32x4* xs) {
 #pragma unroll
-    for (int j = 0; j < XPIECES; ++j) xs[tid + 256 * j] = xreg[j];
+    for (int j = 0; j < XPIECES; ++j) {
+      const int p = tid + 256 * j;
+      const int row = p >> 5, q = p & 31;
+      xs[((row >> 4) * 8 + (q & 7)) * 64 + (((q >> 3) * 16 + (row & 15)) ^ (q & 7))] = xreg[j];
+    }
   }
 
   // plane words, scale and zero of row tile T for the round starting at code kc
@@ -208,7 +215,7 @@ struct SkinnyWave {
     const u32x4 wf1 = w_frag<SLOT, I, 1>();
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const u32x4 xf = xs[(mt * 8 + I) * 64 + lane];
+      const u32x4 xf = xs[(mt * 8 + I) * 64 + (lane ^ I)];
       acc[mt][0] = mfma<BF16>(xf, wf0, acc[mt][0]);
       acc[mt][1] = mfma<BF16>(xf, wf1, acc[mt][1]);
     }
