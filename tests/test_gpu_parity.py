@@ -129,6 +129,7 @@ SHAPES = [
     (33, 200, 1536, 256, "f16"),    # skinny: three m tiles, group 256
     (49, 130, 2304, 128, "bf16"),   # skinny: four m tiles, nine rounds split nine ways
     (64, 17, 4352, 128, "f16"),     # skinny: seventeen rounds, ragged n
+    (12, 384, 3584, 128, "f16"),    # skinny: fourteen rounds split seven ways
     (65, 300, 768, 64, "bf16"),
     (257, 300, 512, 128, "bf16"),
     (300, 448, 1024, 128, "bf16"),  # prefill tile with split k
