@@ -85,7 +85,10 @@ struct GemmTile {
   size_t upr;
   // staging registers: the X tile one k step ahead, the weight planes (from
   // HBM, longer latency) two steps ahead in two slots
-  uint4 xreg[CX];
+  // X staging slots: two (X issued two steps ahead) when the register budget
+  // allows it, i.e. for widths with at most three planes; one otherwise
+  static constexpr int XD = NP <= 3 ? 2 : 1;
+  uint4 xreg[XD][CX];
   uint32_t wrec[2][CW][kUnitWords];
   uint16_t sraw[2][CW], zraw[2][CW];
   floatx4 acc[FM][FN];
@@ -103,6 +106,7 @@ struct GemmTile {
   // read one row's 128-byte k slice, so the vector cache sees one request per
   // row instead of one per lane.  Unconditional loads from clamped addresses:
   // X rows past m only feed output rows that are never stored.
+  template <int XS>
   __device__ __forceinline__ void load_x(int kt) {
     const int k0 = kt * BK;
     const uint16_t* xg = static_cast<const uint16_t*>(a.x);
@@ -111,18 +115,19 @@ struct GemmTile {
       const int c = (tid + i * T) % (BM * 8);
       const int row = c >> 3, col = 8 * (c & 7);
       const int mrow = min(m0 + row, a.m - 1);
-      xreg[i] = *reinterpret_cast<const uint4*>(xg + (size_t)mrow * a.k + k0 + col);
+      xreg[XS % XD][i] = *reinterpret_cast<const uint4*>(xg + (size_t)mrow * a.k + k0 + col);
     }
   }
   // the X tile in LDS is row-major, eight 16-byte chunks per row, with chunk
   // c of row r stored at position c ^ (r % 8): the staging writes (eight
   // lanes per row) and the MFMA fragment reads (sixteen rows, one chunk
   // each) then both spread over all banks
+  template <int XS>
   __device__ __forceinline__ void store_x(uint4* as) {
 #pragma unroll
     for (int i = 0; i < CX; ++i) {
       const int c = tid + i * T;
-      if ((BM * 8) % T == 0 || c < BM * 8) as[(c >> 3) * 8 + ((c & 7) ^ ((c >> 3) & 7))] = xreg[i];
+      if ((BM * 8) % T == 0 || c < BM * 8) as[(c >> 3) * 8 + ((c & 7) ^ ((c >> 3) & 7))] = xreg[XS % XD][i];
     }
   }
   // weight item it -> (row it / 2, unit it % 2): a lane pair reads one row's two
@@ -236,39 +241,43 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs a) {
 
   if (kt_begin < kt_end) {
     const int klast = kt_end - 1;
+    constexpr int XD = Tile::XD;
     t.template load_w<0>(kt_begin);
-    t.load_x(kt_begin);
+    t.template load_x<0>(kt_begin);
     t.template load_w<1>(min(kt_begin + 1, klast));
-    t.store_x(As[0]);
+    if constexpr (XD == 2) t.template load_x<1>(min(kt_begin + 1, klast));
+    t.template store_x<0>(As[0]);
     t.template store_w<0>(Bs[0]);
     __syncthreads();
-    // Two k steps per trip so the LDS buffer and the weight staging slot are
-    // compile-time constants.  Step kt computes from buffer kt & 1, issues X
-    // for kt + 1 and weights for kt + 2 (into the slot that held kt), then
-    // writes step kt + 1 (X registers, weight slot loaded one trip earlier)
-    // into the other buffer.  Past the last step the loads repeat the last
-    // step (in bounds) and nothing more is stored.
+    // Two k steps per trip so the LDS buffer and the staging slots are
+    // compile-time constants.  Step kt computes from buffer kt & 1, issues the
+    // weights for kt + 2 (into the slot that held kt) and X for kt + XD, then
+    // writes step kt + 1 (weights loaded a step earlier, X loaded XD - 1 steps
+    // earlier) into the other buffer.  Past the last step the loads repeat
+    // the last step (in bounds) and nothing more is stored.
     for (int kt = kt_begin; kt < kt_end; kt += 2) {
       {
         const bool has_next = kt + 1 < kt_end;
-        if (has_next) t.load_x(kt + 1);
+        if constexpr (XD == 2) t.template load_x<0>(min(kt + 2, klast));
+        else if (has_next) t.template load_x<0>(kt + 1);
         t.template load_w<0>(min(kt + 2, klast));
         t.mma_half(As[0], Bs[0], 0, lane, wm, wn);
         t.mma_half(As[0], Bs[0], 1, lane, wm, wn);
         if (has_next) {
-          t.store_x(As[1]);
+          t.template store_x<1>(As[1]);
           t.template store_w<1>(Bs[1]);
         }
         __syncthreads();
       }
       if (kt + 1 < kt_end) {
         const bool has_next = kt + 2 < kt_end;
-        if (has_next) t.load_x(kt + 2);
+        if constexpr (XD == 2) t.template load_x<1>(min(kt + 3, klast));
+        else if (has_next) t.template load_x<0>(kt + 2);
         t.template load_w<1>(min(kt + 3, klast));
         t.mma_half(As[1], Bs[1], 0, lane, wm, wn);
         t.mma_half(As[1], Bs[1], 1, lane, wm, wn);
         if (has_next) {
-          t.store_x(As[0]);
+          t.template store_x<0>(As[0]);
           t.template store_w<0>(Bs[0]);
         }
         __syncthreads();
