@@ -314,7 +314,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
-constexpr int kTargetBlocks = 448;  // 1.75 workgroups per CU
+// about one workgroup per CU: measured against 448 and 896 at m = 8 and 64,
+// fewer, longer k ranges win (less split-k traffic, fewer workgroup prologues)
+constexpr int kTargetBlocks = 224;
 
 int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 
