@@ -5,7 +5,9 @@ Workload (one step): the Llama-3.1-8B FFN projections (gate and up 4096->14336,
 down 14336->4096) at decode batch M = 1, fp16 activations, one int8 parent
 per matrix (g = 128, fp16 scale/zero, W ~ N(0, 0.02^2) with 0.1% outliers x10),
 sliced with the true-prefix rule at every width r in {2, 3, 4, 6, 8}: 15 layer
-calls, issued as one mixed-width call per width.
+calls, issued as one mixed-width call per width.  Within such a call the
+library runs the independent gate and up calls (one shape class) as one GEMV
+launch and down as a second one.
 
 Inputs are resident in HBM before timing.  Each step reads a different copy of
 the parents from a ring whose bytes read per pass exceed the 256 MB MALL, so
@@ -18,10 +20,12 @@ steps are replayed from HIP graphs that each hold `ring` consecutive steps in
 the eager order (checked bit for bit against the eager calls before timing),
 which is how a serving loop issues them; `eager` reports the same steps issued
 as one C-ABI call per width, host launch gaps included.  `roofline` is for the
-kernel that takes the most time per step (the r = 8 decode GEMV): its bytes
-per launch over its average launch duration, from HIP events on the launch
-stream around replays of a graph of r = 8 calls only.  `per_r` gives the same
-figure for every width.  `prefill` times the M = 2048 bf16 prefill
+kernel launch that takes the most time per step (the r = 8 GEMV launch that
+serves gate and up together): its bytes per launch over its average launch
+duration, from HIP events on the launch stream around replays of a graph of
+those launches only.  `per_r` gives the same figures for every width and both
+launches of the step, plus the gate call launched alone for comparison.
+`prefill` times the M = 2048 bf16 prefill
 GEMM (same shapes, r in {2, 4, 8}) against the dense bf16 MFMA peak.
 `skinny` times decode batches M in {8, 16, 32, 64} at r in {2, 3, 4, 8} on the
 same shapes against max(HBM time, MFMA time).  `mixnmatch` times one pass over
@@ -54,7 +58,7 @@ METRIC = "sliced W·X: decode GB/s (packed bytes, %HBM peak) + prefill TFLOP/s (
 PLANE_BITS = (2, 1, 1, 2, 2)
 PLANES_FOR_R = {2: 1, 3: 2, 4: 3, 6: 4, 8: 5}
 DECODE_KERNEL_SRC = os.path.join(ROOT, "nested_integer_weight_amd", "csrc", "mq_gemv.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_r8_llama8b_ffn_m1.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_batch_r8_llama8b_gate_up_m1.json")
 
 
 def log(msg):
@@ -144,35 +148,66 @@ def main():
 
     # ---------------- eager timed steps (one C-ABI call per width and step) ----------------
     def eager_run(n_steps, first):
-        ev = {r: [] for r in WIDTHS}
         t0_, t1_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0_.record(stream)
         for i in range(n_steps):
             for r in WIDTHS:
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
                 mq.linear_mixed(calls_for(first + i, r))
-                e1.record(stream)
-                ev[r].append((e0, e1))
         t1_.record(stream)
         torch.cuda.synchronize()
-        return t0_.elapsed_time(t1_), ev
+        return t0_.elapsed_time(t1_)
 
-    eager_ms, ev = eager_run(args.steps, args.warmup)
+    eager_ms = eager_run(args.steps, args.warmup)
     eager = {"value": round(bytes_step * args.steps / (eager_ms * 1e-3) / 1e9, 1),
              "ms_per_step": round(eager_ms / args.steps, 5)}
     log(f"[bench] eager {args.steps} steps: {eager['ms_per_step'] * 1e3:.1f} us/step, {eager['value']} GB/s")
 
-    def per_r_from(ms_of_r, launches):
+    # The step issues two kernel launches per width: mq_linear_mixed runs the
+    # independent gate and up calls (same shape class) as one GEMV launch, and
+    # down as a second one.  Per-launch figures come from graphs (or eager
+    # loops) of one piece at a time, `ring` copies deep.
+    # `gate_alone` (the gate call by itself, one launch) is context: the same
+    # bytes per call without the shared launch.
+    pieces = {"gate_up": [0, 1], "down": [2], "gate_alone": [0]}
+
+    def piece_calls(step, r, idx):
+        allc = calls_for(step, r)
+        return [allc[i] for i in idx]
+
+    def piece_bytes(r, idx):
+        return sum(alg_bytes(1, mats[i]["n"], mats[i]["k"], r) for i in idx)
+
+    def launch_figures(use_graph):
         out = {}
         for r in WIDTHS:
-            per_launch_us = ms_of_r[r] * 1e3 / launches
-            b_launch = bytes_r[r] / len(mats)
-            gbs = b_launch / (per_launch_us * 1e-6) / 1e9
-            out[str(r)] = {"us_per_launch": round(per_launch_us, 3), "bytes_per_launch": int(b_launch),
-                           "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+            out[str(r)] = {}
+            for name, idx in pieces.items():
+                reps = max(1, args.steps // args.ring)
+                if use_graph:
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g):
+                        for i in range(args.ring):
+                            mq.linear_mixed(piece_calls(i, r, idx))
+                    g.replay()
+                    torch.cuda.synchronize()
+                a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a_.record(stream)
+                for _ in range(reps):
+                    if use_graph:
+                        g.replay()
+                    else:
+                        for i in range(args.ring):
+                            mq.linear_mixed(piece_calls(i, r, idx))
+                b_.record(stream)
+                torch.cuda.synchronize()
+                us = a_.elapsed_time(b_) * 1e3 / (reps * args.ring)
+                byt = piece_bytes(r, idx)
+                gbs = byt / (us * 1e-6) / 1e9
+                out[str(r)][name] = {"us_per_launch": round(us, 3), "bytes_per_launch": int(byt),
+                                     "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+                if use_graph:
+                    del g
         return out
 
     # ---------------- HIP graph replay (the serving form of the step) ----------------
@@ -180,7 +215,6 @@ def main():
     # parent copies, so each replay still reads every weight byte from HBM; the
     # host issues one launch per `ring` steps instead of one call per width.
     mode = "eager"
-    per_r = per_r_from({r: float(np.mean([a.elapsed_time(b) for a, b in ev[r]])) for r in WIDTHS}, len(mats))
     value, ms_per_step, timed_steps = eager["value"], eager["ms_per_step"], args.steps
     if not args.eager:
         ring = args.ring
@@ -202,13 +236,6 @@ def main():
                 for i in range(rem):
                     for r in WIDTHS:
                         mq.linear_mixed(calls_for(i, r))
-        g_r = {}
-        for r in WIDTHS:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for i in range(ring):
-                    mq.linear_mixed(calls_for(i, r))
-            g_r[r] = g
         ok = True
         for rep in range(2):  # replays interleaved with eager work and synchronisation
             for mt in mats:
@@ -235,23 +262,11 @@ def main():
             g_ms = t0_.elapsed_time(t1_)
             ms_per_step = g_ms / timed_steps
             value = bytes_step * timed_steps / (g_ms * 1e-3) / 1e9
-            ms_r = {}
-            for r in WIDTHS:
-                g_r[r].replay()
-                torch.cuda.synchronize()
-                a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                reps_r = max(1, reps)
-                a_.record(stream)
-                for _ in range(reps_r):
-                    g_r[r].replay()
-                b_.record(stream)
-                torch.cuda.synchronize()
-                ms_r[r] = a_.elapsed_time(b_) / reps_r / ring
-            per_r = per_r_from(ms_r, len(mats))
             mode = "hip_graph"
             log(f"[bench] graph {timed_steps} steps: {ms_per_step * 1e3:.1f} us/step, {value:.1f} GB/s")
-        del g_step, g_r, g_rem
-    dom = per_r["8"]
+        del g_step, g_rem
+    per_r = launch_figures(mode == "hip_graph")
+    dom = per_r["8"]["gate_up"]
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -264,7 +279,8 @@ def main():
 
     roofline = {"bound": "hbm", "achieved": dom["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(dom["GB/s"] / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "mq::gemv_kernel<r=8, prefix, m=1, fp16> (mq_linear decode path)",
+                "kernel": "mq::gemv_batch_kernel<r=8, prefix, m=1, fp16>: gate and up (2 x 14336x4096) in one "
+                          "launch (mq_linear_mixed decode path)",
                 "bytes_per_launch": dom["bytes_per_launch"], "us_per_launch": dom["us_per_launch"]}
 
     # ---------------- prefill (M = 2048, bf16) ----------------
@@ -437,7 +453,7 @@ def main():
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": timed_steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
-        "config": {"workload": "llama3.1-8b-ffn decode: gate/up 4096->14336 + down 14336->4096, M=1, "
+        "config": {"workload": "llama3.1-8b-ffn decode: gate/up 4096->14336 (one launch) + down 14336->4096, M=1, "
                                "g=128, true-prefix, r in {2,3,4,6,8}",
                    "global_batch": 1, "widths": list(WIDTHS), "ring_copies": args.ring},
         "roofline": roofline,

@@ -154,7 +154,12 @@ mq_status mq_linear(const void* x, int32_t x_dtype, int32_t m, const mq_packed* 
  * layer matrices, each at its own width, issued in order on one stream and
  * sharing one workspace.  All calls are validated before the first launch; an
  * invalid call returns its status and nothing is launched.  *failed_call (if
- * not NULL) receives the index of the first invalid call, else -1. */
+ * not NULL) receives the index of the first invalid call, else -1.
+ * Consecutive calls that take the register GEMV with the same m, k, width,
+ * rule, group and dtype, and whose outputs overlap neither each other nor the
+ * others' inputs, run in one launch (up to 4 calls; e.g. the gate and up
+ * projections of a decode step).  The results are those of issuing the calls
+ * in order; a launch error reports the first call of its launch. */
 mq_status mq_linear_mixed(const mq_call* calls, int32_t n_calls, void* workspace,
                           size_t workspace_bytes, int32_t* failed_call, void* stream);
 

@@ -99,6 +99,44 @@ mq_status run_linear(const void* x, int x_dtype, int m, const mq_packed* w, int 
   return e == hipSuccess ? MQ_OK : MQ_EHIP;
 }
 
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return na && nb && a0 < b0 + nb && b0 < a0 + na;
+}
+
+size_t x_bytes(const mq_call& c) { return (size_t)c.m * (size_t)c.w->k * 2; }
+size_t y_bytes(const mq_call& c) { return (size_t)c.m * (size_t)c.w->n * 2; }
+
+// May call d join a single GEMV launch with call c (c issued before d)?  They
+// must share the shape class of the launch (m, k, width, rule, group, dtype)
+// and be independent: neither output may overlap the other call's input or
+// output, so running both at once gives what running them in order gives.
+bool can_batch(const mq_call& c, const mq_call& d) {
+  if (c.m != d.m || c.m == 0 || c.w->k != d.w->k || c.r != d.r || c.rule != d.rule || c.group != d.group ||
+      c.x_dtype != d.x_dtype)
+    return false;
+  if (!gemv_eligible(c.m, c.w->k, c.x_dtype == MQ_BF16)) return false;
+  return !overlaps(c.y, y_bytes(c), d.x, x_bytes(d)) && !overlaps(d.y, y_bytes(d), c.x, x_bytes(c)) &&
+         !overlaps(c.y, y_bytes(c), d.y, y_bytes(d));
+}
+
+LinearArgs gemv_args(const mq_call& c, const PlanePtrs& pl) {
+  LinearArgs a;
+  a.x = c.x;
+  a.y = c.y;
+  a.pl = pl;
+  a.scales = c.scales;
+  a.zeros = c.zeros;
+  a.m = c.m;
+  a.n = c.w->n;
+  a.k = c.w->k;
+  a.group = c.group;
+  a.r = c.r;
+  a.round_rule = c.rule == MQ_ROUND;
+  a.bf16 = c.x_dtype == MQ_BF16;
+  return a;
+}
+
 }  // namespace
 
 extern "C" {
@@ -176,16 +214,37 @@ mq_status mq_linear_mixed(const mq_call* calls, int32_t n_calls, void* workspace
       return st;
     }
   }
-  for (int32_t i = 0; i < n_calls; ++i) {
+  for (int32_t i = 0; i < n_calls;) {
     const mq_call& c = calls[i];
     PlanePtrs pl;
     validate_linear(c.x, c.x_dtype, c.m, c.w, c.r, c.rule, c.group, c.scales, c.zeros, c.y, &pl);
-    mq_status st = run_linear(c.x, c.x_dtype, c.m, c.w, c.r, c.rule, c.group, c.scales, c.zeros, c.y, workspace,
-                              workspace_bytes, pl, static_cast<hipStream_t>(stream));
+    // consecutive independent GEMV calls of one shape class share a launch
+    int32_t j = i + 1;
+    while (j < n_calls && j - i < kGemvMaxBatch) {
+      bool ok = true;
+      for (int32_t t = i; t < j && ok; ++t) ok = can_batch(calls[t], calls[j]);
+      if (!ok) break;
+      ++j;
+    }
+    mq_status st;
+    if (j - i > 1) {
+      LinearArgs la[kGemvMaxBatch];
+      for (int32_t t = i; t < j; ++t) {
+        PlanePtrs plt;
+        const mq_call& ct = calls[t];
+        validate_linear(ct.x, ct.x_dtype, ct.m, ct.w, ct.r, ct.rule, ct.group, ct.scales, ct.zeros, ct.y, &plt);
+        la[t - i] = gemv_args(ct, plt);
+      }
+      st = launch_gemv_batch(la, j - i, static_cast<hipStream_t>(stream)) == hipSuccess ? MQ_OK : MQ_EHIP;
+    } else {
+      st = run_linear(c.x, c.x_dtype, c.m, c.w, c.r, c.rule, c.group, c.scales, c.zeros, c.y, workspace,
+                      workspace_bytes, pl, static_cast<hipStream_t>(stream));
+    }
     if (st != MQ_OK) {
       if (failed_call) *failed_call = i;
       return st;
     }
+    i = j;
   }
   return MQ_OK;
 }

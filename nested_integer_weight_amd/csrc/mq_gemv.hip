@@ -102,7 +102,7 @@ __device__ __forceinline__ float dot2h(uint32_t a, uint32_t b, float c) {
 // its quad for row t) and DPP quad broadcasts hand every lane its own value;
 // otherwise each row costs two 16-bit loads per lane.
 template <int R, int ROUND, int MT, int BF16, int ROWS, int SZ4>
-__global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
+__device__ __forceinline__ void gemv_body(const GemvArgs a, const unsigned blk) {
   constexpr int NP = planes_needed(R, ROUND);
   // width 2, true prefix, fp16: fields go straight from the plane-0 word to
   // fp16 with one and-or per pair (no byte assembly)
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   const size_t upr = (size_t)(a.k >> 5);  // units per row
   const int gpr = a.k / a.group;
   const int gidx = (slice * 64) / a.group;
-  const size_t row0 = (size_t)blockIdx.x * (size_t)ROWS;
+  const size_t row0 = (size_t)blk * (size_t)ROWS;
 
   // ---- 1. issue the activation loads of this slice ----
   // (unconditional loads from clamped addresses; invalid lanes/tokens are
@@ -390,53 +390,97 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   }
 }
 
+template <int R, int ROUND, int MT, int BF16, int ROWS, int SZ4>
+__global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
+  gemv_body<R, ROUND, MT, BF16, ROWS, SZ4>(a, blockIdx.x);
+}
+
+// Several independent calls of one shape class (same m, k, width, rule,
+// group, dtype) in one launch: workgroup b serves the call whose block range
+// holds b.  One launch then streams the bytes of all of them, so the launch
+// ramp and drain are paid once.
+struct GemvBatch {
+  GemvArgs call[kGemvMaxBatch];
+  int first_block[kGemvMaxBatch];  // first workgroup of each call
+  int ncalls;
+};
+
+template <int R, int ROUND, int MT, int BF16, int ROWS, int SZ4>
+__global__ __launch_bounds__(256) void gemv_batch_kernel(GemvBatch b) {
+  int c = 0;
+#pragma unroll
+  for (int i = 1; i < kGemvMaxBatch; ++i)
+    if (i < b.ncalls && (int)blockIdx.x >= b.first_block[i]) c = i;
+  gemv_body<R, ROUND, MT, BF16, ROWS, SZ4>(b.call[c], blockIdx.x - (unsigned)b.first_block[c]);
+}
+
 template <int R, int ROUND, int MT, int BF16>
-static hipError_t gemv_launch_t(const LinearArgs& la, hipStream_t s) {
+static hipError_t gemv_launch_t(const LinearArgs* la, int ncalls, hipStream_t s) {
   constexpr int ROWS = (MT >= 4) ? 4 : 8;
-  GemvArgs a;
-  a.x = la.x;
-  a.y = la.y;
-  a.pl = la.pl;
-  a.scales = la.scales;
-  a.zeros = la.zeros;
-  a.m = la.m;
-  a.n = la.n;
-  a.k = la.k;
-  a.group = la.group;
-  const int S = la.k / 64;
+  GemvBatch b;
+  unsigned blocks = 0;
+  for (int i = 0; i < ncalls; ++i) {
+    GemvArgs& a = b.call[i];
+    a.x = la[i].x;
+    a.y = la[i].y;
+    a.pl = la[i].pl;
+    a.scales = la[i].scales;
+    a.zeros = la[i].zeros;
+    a.m = la[i].m;
+    a.n = la[i].n;
+    a.k = la[i].k;
+    a.group = la[i].group;
+    b.first_block[i] = (int)blocks;
+    blocks += (unsigned)((la[i].n + ROWS - 1) / ROWS);
+  }
+  for (int i = ncalls; i < kGemvMaxBatch; ++i) {
+    b.call[i] = b.call[0];
+    b.first_block[i] = (int)blocks;
+  }
+  b.ncalls = ncalls;
+  // every call of a batch shares k and group, hence the workgroup shape
+  const int S = la[0].k / 64;
   const int threads = ((S + 63) / 64) * 64;  // one lane per 64-code slice, whole waves
-  const unsigned blocks = (unsigned)((la.n + ROWS - 1) / ROWS);
   const size_t lds = (threads > 64) ? (size_t)(threads / 64) * ROWS * MT * sizeof(float) : 0;
-  const int gpr = la.k / la.group;
-  if (la.group == 128 && gpr % 2 == 0)
-    hipLaunchKernelGGL((gemv_kernel<R, ROUND, MT, BF16, ROWS, 1>), dim3(blocks), dim3(threads), lds, s, a);
-  else
-    hipLaunchKernelGGL((gemv_kernel<R, ROUND, MT, BF16, ROWS, 0>), dim3(blocks), dim3(threads), lds, s, a);
+  const int gpr = la[0].k / la[0].group;
+  const bool sz4 = la[0].group == 128 && gpr % 2 == 0;
+  if (ncalls == 1) {
+    if (sz4)
+      hipLaunchKernelGGL((gemv_kernel<R, ROUND, MT, BF16, ROWS, 1>), dim3(blocks), dim3(threads), lds, s, b.call[0]);
+    else
+      hipLaunchKernelGGL((gemv_kernel<R, ROUND, MT, BF16, ROWS, 0>), dim3(blocks), dim3(threads), lds, s, b.call[0]);
+  } else {
+    if (sz4)
+      hipLaunchKernelGGL((gemv_batch_kernel<R, ROUND, MT, BF16, ROWS, 1>), dim3(blocks), dim3(threads), lds, s, b);
+    else
+      hipLaunchKernelGGL((gemv_batch_kernel<R, ROUND, MT, BF16, ROWS, 0>), dim3(blocks), dim3(threads), lds, s, b);
+  }
   return hipGetLastError();
 }
 
 template <int R, int ROUND, int BF16>
-static hipError_t gemv_launch_m(const LinearArgs& a, hipStream_t s) {
+static hipError_t gemv_launch_m(const LinearArgs* a, int n, hipStream_t s) {
   if constexpr (BF16) {
-    return gemv_launch_t<R, ROUND, 1, 1>(a, s);  // bf16: m == 1 only
+    return gemv_launch_t<R, ROUND, 1, 1>(a, n, s);  // bf16: m == 1 only
   } else {
-    switch (a.m) {
-      case 1: return gemv_launch_t<R, ROUND, 1, 0>(a, s);
-      case 2: return gemv_launch_t<R, ROUND, 2, 0>(a, s);
-      default: return gemv_launch_t<R, ROUND, 4, 0>(a, s);
+    switch (a[0].m) {
+      case 1: return gemv_launch_t<R, ROUND, 1, 0>(a, n, s);
+      case 2: return gemv_launch_t<R, ROUND, 2, 0>(a, n, s);
+      default: return gemv_launch_t<R, ROUND, 4, 0>(a, n, s);
     }
   }
 }
 
 template <int R, int ROUND>
-static hipError_t gemv_launch_d(const LinearArgs& a, hipStream_t s) {
-  return a.bf16 ? gemv_launch_m<R, ROUND, 1>(a, s) : gemv_launch_m<R, ROUND, 0>(a, s);
+static hipError_t gemv_launch_d(const LinearArgs* a, int n, hipStream_t s) {
+  return a[0].bf16 ? gemv_launch_m<R, ROUND, 1>(a, n, s) : gemv_launch_m<R, ROUND, 0>(a, n, s);
 }
 
-hipError_t launch_gemv(const LinearArgs& a, hipStream_t s) {
+hipError_t launch_gemv_batch(const LinearArgs* a, int ncalls, hipStream_t s) {
+  if (ncalls < 1 || ncalls > kGemvMaxBatch) return hipErrorInvalidValue;
 #define MQ_GEMV_CASE(RR) \
-  case RR: return a.round_rule ? gemv_launch_d<RR, 1>(a, s) : gemv_launch_d<RR, 0>(a, s);
-  switch (a.r) {
+  case RR: return a[0].round_rule ? gemv_launch_d<RR, 1>(a, ncalls, s) : gemv_launch_d<RR, 0>(a, ncalls, s);
+  switch (a[0].r) {
     MQ_GEMV_CASE(2)
     MQ_GEMV_CASE(3)
     MQ_GEMV_CASE(4)
@@ -446,5 +490,7 @@ hipError_t launch_gemv(const LinearArgs& a, hipStream_t s) {
   }
 #undef MQ_GEMV_CASE
 }
+
+hipError_t launch_gemv(const LinearArgs& a, hipStream_t s) { return launch_gemv_batch(&a, 1, s); }
 
 }  // namespace mq

@@ -187,6 +187,60 @@ def test_mixed_equals_single_calls(mq):
         check_y(y, lay, lay.x, c.r, c.rule)
 
 
+@pytest.mark.parametrize("m,dt,r,rule,group", [(1, "f16", 2, O.PREFIX, 128), (3, "f16", 3, O.ROUND, 64),
+                                                (1, "bf16", 8, O.PREFIX, 128), (2, "f16", 6, O.PREFIX, 256)])
+def test_mixed_batches_independent_gemv_calls(mq, m, dt, r, rule, group):
+    # five independent calls of one shape class with ragged n: the library runs
+    # the first four in one launch and the fifth alone; each result must equal
+    # its single call bit for bit and the oracle within tolerance
+    calls, lays = [], []
+    for i, n in enumerate((1, 70, 333, 8, 1025)):
+        lay = synth.make_layer(cfg_id=5, tensor_id=300 + 10 * i + r, n=n, k=1024, m=m, group=group, x_dtype=dt)
+        q, s, z = to_dev(lay)
+        calls.append(mq.Call(x=lay.x.to(DEV), packed=mq.pack_parent(q), r=r, rule=rule, group=group,
+                             scales=s, zeros=z))
+        lays.append(lay)
+    outs = mq.linear_mixed(calls)
+    for c, lay, y in zip(calls, lays, outs):
+        single = mq.linear(c.x, c.packed, c.r, c.rule, c.group, c.scales, c.zeros)
+        assert torch.equal(single, y)
+        check_y(y, lay, lay.x, c.r, c.rule)
+
+
+def test_mixed_dependent_gemv_calls_keep_order(mq):
+    # same shape class throughout (m = 1, k = n = 512), but B reads A's output,
+    # C overwrites A's output and D is independent: the result must be that of
+    # the calls issued one by one
+    k = 512
+    lays, packs = [], []
+    for i in range(4):
+        lay = synth.make_layer(cfg_id=5, tensor_id=400 + i, n=k, k=k, m=1, group=128, x_dtype="f16")
+        q, s, z = to_dev(lay)
+        lays.append(lay)
+        packs.append((mq.pack_parent(q), s, z))
+    x0 = lays[0].x.to(DEV)
+    x3 = lays[3].x.to(DEV)
+    ya = torch.empty((1, k), dtype=torch.float16, device=DEV)
+    yb = torch.empty((1, k), dtype=torch.float16, device=DEV)
+    yd = torch.empty((1, k), dtype=torch.float16, device=DEV)
+
+    def calls():
+        return [mq.Call(x=x0, packed=packs[0][0], r=4, rule=O.PREFIX, group=128, scales=packs[0][1],
+                        zeros=packs[0][2], out=ya),
+                mq.Call(x=ya, packed=packs[1][0], r=4, rule=O.PREFIX, group=128, scales=packs[1][1],
+                        zeros=packs[1][2], out=yb),
+                mq.Call(x=x3, packed=packs[2][0], r=4, rule=O.PREFIX, group=128, scales=packs[2][1],
+                        zeros=packs[2][2], out=ya),
+                mq.Call(x=x3, packed=packs[3][0], r=4, rule=O.PREFIX, group=128, scales=packs[3][1],
+                        zeros=packs[3][2], out=yd)]
+
+    mq.linear_mixed(calls())
+    got = [ya.clone(), yb.clone(), yd.clone()]
+    for c in calls():
+        mq.linear(c.x, c.packed, c.r, c.rule, c.group, c.scales, c.zeros, out=c.out)
+    assert torch.equal(got[0], ya) and torch.equal(got[1], yb) and torch.equal(got[2], yd)
+
+
 # ---------------------------------------------------------------------------
 # full workload shapes, sampled rows
 # ---------------------------------------------------------------------------
