@@ -49,6 +49,7 @@ __host__ inline bool skinny_eligible(int m, int k) { return m >= 2 && m <= kSkin
 struct SkinnyPlan {
   int splits;            // k ranges (1 = no workspace)
   int rounds_per_split;  // 256-wide k rounds per range
+  int nt;                // 16-row tiles per wave: 1 (64-row workgroups) or 2 (128-row)
 };
 SkinnyPlan plan_skinny(int m, int n, int k);
 size_t skinny_workspace_bytes(int m, int n, int k);

@@ -49,8 +49,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
-constexpr int kNT = 2;                        // 16-row output tiles per wave
-constexpr int kColsPerBlock = 16 * kNT * kWaves;  // 128
+// 16-row output tiles per wave: NT = 2 (128 output rows per workgroup) or
+// NT = 1 (64 rows, for wide n: enough workgroups without splitting k)
+template <int NT>
+constexpr int cols_per_block() { return 16 * NT * kWaves; }
 constexpr int kRound = 256;                   // k per round
 
 struct SkinnyArgs {
@@ -85,7 +87,7 @@ __device__ __forceinline__ uint32_t dq_f16x2(uint32_t magic_pair, f16x2 c, f16x2
   return __builtin_bit_cast(uint32_t, v);
 }
 
-template <int R, int ROUND, int BF16, int MT>
+template <int R, int ROUND, int BF16, int MT, int NT>
 struct SkinnyWave {
   static constexpr int NP = planes_needed(R, ROUND);
   static constexpr float kDelta = ROUND ? 0.0f : prefix_delta(R);
@@ -100,24 +102,24 @@ struct SkinnyWave {
   size_t upr;
   int gpr;
   // weights of one round per slot: [slot][tile][unit][word]
-  uint32_t rec[kSlots][kNT][2][kUnitWords];
+  uint32_t rec[kSlots][NT][2][kUnitWords];
   // raw fp16 bits of scale and zero, zero-extended by the load itself (no
   // arithmetic before use, so the loads stay in flight)
-  uint32_t sraw[kSlots][kNT], zraw[kSlots][kNT];
+  uint32_t sraw[kSlots][NT], zraw[kSlots][NT];
   u32x4 xreg[XPIECES];
-  f32x4 acc[MT][kNT];
+  f32x4 acc[MT][NT];
 
   __device__ __forceinline__ SkinnyWave(const SkinnyArgs& args, int t, int n0, int kbase) : a(args), tid(t), kb0(kbase) {
     lane = t & 63;
     g = lane >> 4;
     c = lane & 15;
-    nw = n0 + 32 * (t >> 6);
+    nw = n0 + 16 * NT * (t >> 6);
     upr = (size_t)(a.k >> 5);
     gpr = a.k / a.group;
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
-      for (int j = 0; j < kNT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   // X piece p = tid + 256 j is 16-byte chunk q = p % 32 of row p / 32 of the
@@ -172,9 +174,8 @@ struct SkinnyWave {
   template <int SLOT>
   __device__ __forceinline__ void load_w(int rnd) {
     const int kc = kb0 + rnd * kRound + 64 * g;  // first code of this lane's chunk
-    static_assert(kNT == 2, "two row tiles per wave");
     load_w_tile<SLOT, 0>(kc);
-    load_w_tile<SLOT, 1>(kc);
+    if constexpr (NT == 2) load_w_tile<SLOT, 1>(kc);
   }
 
   // weight operand of MFMA k-step I for row tile T: codes [8 I, 8 I + 8) of the chunk
@@ -211,13 +212,22 @@ struct SkinnyWave {
 
   template <int SLOT, int I>
   __device__ __forceinline__ void kstep(const u32x4* xs) {
-    const u32x4 wf0 = w_frag<SLOT, I, 0>();
-    const u32x4 wf1 = w_frag<SLOT, I, 1>();
+    if constexpr (NT == 2) {
+      const u32x4 wf0 = w_frag<SLOT, I, 0>();
+      const u32x4 wf1 = w_frag<SLOT, I, NT - 1>();
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const u32x4 xf = xs[(mt * 8 + I) * 64 + (lane ^ I)];
-      acc[mt][0] = mfma<BF16>(xf, wf0, acc[mt][0]);
-      acc[mt][1] = mfma<BF16>(xf, wf1, acc[mt][1]);
+      for (int mt = 0; mt < MT; ++mt) {
+        const u32x4 xf = xs[(mt * 8 + I) * 64 + (lane ^ I)];
+        acc[mt][0] = mfma<BF16>(xf, wf0, acc[mt][0]);
+        acc[mt][NT - 1] = mfma<BF16>(xf, wf1, acc[mt][NT - 1]);
+      }
+    } else {
+      const u32x4 wf0 = w_frag<SLOT, I, 0>();
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const u32x4 xf = xs[(mt * 8 + I) * 64 + (lane ^ I)];
+        acc[mt][0] = mfma<BF16>(xf, wf0, acc[mt][0]);
+      }
     }
   }
 
@@ -278,24 +288,24 @@ struct SkinnyWave {
 
 // Two waves per SIMD is enough to cover the latency with the prefetch above;
 // asking for more would make the compiler spill the staging registers.
-template <int R, int ROUND, int BF16, int MT>
+template <int R, int ROUND, int BF16, int MT, int NT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void skinny_kernel(SkinnyArgs a) {
   __shared__ u32x4 Xs0[MT * 8 * 64];
   __shared__ u32x4 Xs1[MT * 8 * 64];
   const int tid = threadIdx.x;
-  const int n0 = blockIdx.x * kColsPerBlock;
+  const int n0 = blockIdx.x * cols_per_block<NT>();
   const int kb0 = blockIdx.y * a.rounds_per_split * kRound;
   const int nr = min(a.rounds_per_split, (a.k - kb0) / kRound);
-  SkinnyWave<R, ROUND, BF16, MT> w(a, tid, n0, kb0);
+  SkinnyWave<R, ROUND, BF16, MT, NT> w(a, tid, n0, kb0);
   if (nr > 0) w.run(nr, Xs0, Xs1);
   // lane holds D[4 (lane / 16) + v][lane % 16] of every (m tile, row tile)
   const int lane = tid & 63;
-  const int nb = n0 + 32 * (tid >> 6) + (lane & 15);
+  const int nb = n0 + 16 * NT * (tid >> 6) + (lane & 15);
   const int mb = 4 * (lane >> 4);
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-    for (int t = 0; t < kNT; ++t) {
+    for (int t = 0; t < NT; ++t) {
       const int nn = nb + 16 * t;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
@@ -320,20 +330,21 @@ constexpr int kTargetBlocks = 224;
 
 int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 
-template <int R, int ROUND, int BF16>
+template <int R, int ROUND, int BF16, int NT>
 hipError_t launch_t(const SkinnyArgs& sa, int mt, dim3 grid, hipStream_t s) {
   switch (mt) {
-    case 1: hipLaunchKernelGGL((skinny_kernel<R, ROUND, BF16, 1>), grid, dim3(256), 0, s, sa); break;
-    case 2: hipLaunchKernelGGL((skinny_kernel<R, ROUND, BF16, 2>), grid, dim3(256), 0, s, sa); break;
-    case 3: hipLaunchKernelGGL((skinny_kernel<R, ROUND, BF16, 3>), grid, dim3(256), 0, s, sa); break;
-    default: hipLaunchKernelGGL((skinny_kernel<R, ROUND, BF16, 4>), grid, dim3(256), 0, s, sa); break;
+    case 1: hipLaunchKernelGGL((skinny_kernel<R, ROUND, BF16, 1, NT>), grid, dim3(256), 0, s, sa); break;
+    case 2: hipLaunchKernelGGL((skinny_kernel<R, ROUND, BF16, 2, NT>), grid, dim3(256), 0, s, sa); break;
+    case 3: hipLaunchKernelGGL((skinny_kernel<R, ROUND, BF16, 3, NT>), grid, dim3(256), 0, s, sa); break;
+    default: hipLaunchKernelGGL((skinny_kernel<R, ROUND, BF16, 4, NT>), grid, dim3(256), 0, s, sa); break;
   }
   return hipGetLastError();
 }
 
 template <int R, int ROUND>
-hipError_t launch_d(const SkinnyArgs& sa, int bf16, int mt, dim3 grid, hipStream_t s) {
-  return bf16 ? launch_t<R, ROUND, 1>(sa, mt, grid, s) : launch_t<R, ROUND, 0>(sa, mt, grid, s);
+hipError_t launch_d(const SkinnyArgs& sa, int bf16, int mt, int nt, dim3 grid, hipStream_t s) {
+  if (nt == 1) return bf16 ? launch_t<R, ROUND, 1, 1>(sa, mt, grid, s) : launch_t<R, ROUND, 0, 1>(sa, mt, grid, s);
+  return bf16 ? launch_t<R, ROUND, 1, 2>(sa, mt, grid, s) : launch_t<R, ROUND, 0, 2>(sa, mt, grid, s);
 }
 
 }  // namespace
@@ -341,7 +352,10 @@ hipError_t launch_d(const SkinnyArgs& sa, int bf16, int mt, dim3 grid, hipStream
 SkinnyPlan plan_skinny(int m, int n, int k) {
   SkinnyPlan p;
   const int rounds = k / kRound;
-  const int blocks_n = cdiv(n, kColsPerBlock);
+  // 64-row workgroups when they alone give the target count (no split-k and
+  // no reduction launch); otherwise 128-row workgroups with k split
+  p.nt = cdiv(n, cols_per_block<1>()) >= kTargetBlocks ? 1 : 2;
+  const int blocks_n = p.nt == 1 ? cdiv(n, cols_per_block<1>()) : cdiv(n, cols_per_block<2>());
   int s = cdiv(kTargetBlocks, blocks_n);
   if (s > rounds) s = rounds;
   if (s < 1) s = 1;
@@ -376,11 +390,12 @@ hipError_t launch_skinny(const LinearArgs& la, void* workspace, size_t workspace
   sa.to_workspace = p.splits > 1;
   sa.y = p.splits > 1 ? workspace : la.y;
   const int mt = cdiv(la.m, 16);
-  const dim3 grid((unsigned)cdiv(la.n, kColsPerBlock), (unsigned)p.splits);
+  const dim3 grid((unsigned)cdiv(la.n, p.nt == 1 ? cols_per_block<1>() : cols_per_block<2>()), (unsigned)p.splits);
   hipError_t e;
 #define MQ_SK_CASE(RR)                                                                               \
   case RR:                                                                                           \
-    e = la.round_rule ? launch_d<RR, 1>(sa, la.bf16, mt, grid, s) : launch_d<RR, 0>(sa, la.bf16, mt, grid, s); \
+    e = la.round_rule ? launch_d<RR, 1>(sa, la.bf16, mt, p.nt, grid, s)                           \
+                      : launch_d<RR, 0>(sa, la.bf16, mt, p.nt, grid, s);                          \
     break;
   switch (la.r) {
     MQ_SK_CASE(2)

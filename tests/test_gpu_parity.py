@@ -130,6 +130,8 @@ SHAPES = [
     (49, 130, 2304, 128, "bf16"),   # skinny: four m tiles, nine rounds split nine ways
     (64, 17, 4352, 128, "f16"),     # skinny: seventeen rounds, ragged n
     (12, 384, 3584, 128, "f16"),    # skinny: fourteen rounds split seven ways
+    (5, 14400, 512, 64, "f16"),     # skinny with 64-row workgroups (wide n, no k split)
+    (20, 14337, 256, 128, "bf16"),  # skinny 64-row workgroups, two m tiles, one-row tail block
     (65, 300, 768, 64, "bf16"),
     (257, 300, 512, 128, "bf16"),
     (300, 448, 1024, 128, "bf16"),  # prefill tile with split k
