@@ -95,7 +95,9 @@ struct SkinnyWave {
 
   // weight slots in flight: rounds with few planes carry little data, so they
   // are loaded two rounds ahead; wider ones one round ahead
-  static constexpr int kSlots = NP <= 3 ? 3 : 2;
+  // (bf16 at one m tile with two row tiles is the exception: its fp32 operand
+  // arithmetic leaves no room for a third slot without spilling)
+  static constexpr int kSlots = (NP <= 3 && !(BF16 && MT == 1 && NT == 2)) ? 3 : 2;
 
   const SkinnyArgs a;  // by value: a reference would make the compiler keep a copy in memory
   int tid, lane, g, c, nw, kb0;
