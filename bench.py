@@ -16,10 +16,11 @@ weight reads come from HBM, not the last-level cache.
 Printed JSON (one line): value = algorithmic bytes of all calls / wall time of
 the timed steps (GB/s).  Algorithmic bytes per call = bit planes the width
 reads + 4 B (fp16 scale + zero) per group + X (2*M*K) + Y (2*M*N).  The timed
-steps are replayed from HIP graphs that each hold `ring` consecutive steps in
-the eager order (checked bit for bit against the eager calls before timing),
-which is how a serving loop issues them; `eager` reports the same steps issued
-as one C-ABI call per width, host launch gaps included.  `roofline` is for the
+steps are timed twice: replayed from HIP graphs that each hold `ring`
+consecutive steps in the eager order (checked bit for bit against the eager
+calls before timing), and issued as one C-ABI call per width (`eager`, host
+launch gaps included); `graph` and `eager` are both reported and `value` is the
+faster of the two (`timing` names it).  `roofline` is for the
 kernel launch that takes the most time per step (the r = 8 GEMV launch that
 serves gate and up together): its bytes per launch over its average launch
 duration, from HIP events on the launch stream around replays of a graph of
@@ -214,8 +215,8 @@ def main():
     # One graph holds `ring` consecutive steps in the eager order of widths and
     # parent copies, so each replay still reads every weight byte from HBM; the
     # host issues one launch per `ring` steps instead of one call per width.
-    mode = "eager"
-    value, ms_per_step, timed_steps = eager["value"], eager["ms_per_step"], args.steps
+    graph, graph_ok = None, False
+    timed_steps = args.steps
     if not args.eager:
         ring = args.ring
         # eager reference of the last step of the ring, then the graph's last step must match it
@@ -260,12 +261,19 @@ def main():
             t1_.record(stream)
             torch.cuda.synchronize()
             g_ms = t0_.elapsed_time(t1_)
-            ms_per_step = g_ms / timed_steps
-            value = bytes_step * timed_steps / (g_ms * 1e-3) / 1e9
-            mode = "hip_graph"
-            log(f"[bench] graph {timed_steps} steps: {ms_per_step * 1e3:.1f} us/step, {value:.1f} GB/s")
+            graph = {"value": round(bytes_step * timed_steps / (g_ms * 1e-3) / 1e9, 1),
+                     "ms_per_step": round(g_ms / timed_steps, 5)}
+            graph_ok = True
+            log(f"[bench] graph {timed_steps} steps: {graph['ms_per_step'] * 1e3:.1f} us/step, {graph['value']} GB/s")
         del g_step, g_rem
-    per_r = launch_figures(mode == "hip_graph")
+    # `value`: the faster of the two issue forms of the same timed steps (both
+    # reported); with two launches per width the host keeps ahead of the GPU,
+    # so eager calls and graph replay take about the same time
+    if graph is not None and graph["value"] >= eager["value"]:
+        mode, value, ms_per_step = "hip_graph", graph["value"], graph["ms_per_step"]
+    else:
+        mode, value, ms_per_step = "eager", eager["value"], eager["ms_per_step"]
+    per_r = launch_figures(graph_ok)
     dom = per_r["8"]["gate_up"]
 
     traffic = None
@@ -459,6 +467,7 @@ def main():
         "roofline": roofline,
         "timing": mode,
         "eager": eager,
+        "graph": graph,
         "per_r": per_r,
         "prefill": prefill,
         "skinny": skinny,
