@@ -119,6 +119,9 @@ SHAPES = [
     (4, 65, 4096, 128, "f16"),
     (1, 96, 14336, 128, "f16"),
     (1, 40, 20480, 128, "f16"),     # k beyond the register GEMV: MFMA path at m = 1
+    (1, 33, 16384, 128, "bf16"),    # k at the register GEMV's limit (four waves per row)
+    (3, 40, 512, 512, "f16"),       # one quantization group per row
+    (24, 72, 1024, 1024, "f16"),    # skinny with one group per row
     (2, 50, 1024, 64, "bf16"),
     (5, 300, 640, 128, "f16"),
     (8, 257, 1024, 64, "f16"),
