@@ -374,8 +374,11 @@ def main():
         mix = {"widths": widths, "mean_bits": sum(widths) / len(widths)}
         for m, dt, tdt in ((1, "f16", torch.float16), (256, "bf16", torch.bfloat16)):
             xk = {k: synth.activations(synth.rng_for(5, 77, k, m), m, k, dt).to(dev) for k in (3584, 14336)}
-            yn = {n: torch.empty((m, n), dtype=tdt, device=dev) for n in (3584, 14336)}
-            calls = [mq.Call(x=xk[k], packed=pk, r=r, rule="prefix", group=GROUP, scales=s_, zeros=z_, out=yn[n])
+            # each projection writes its own output, as in an FFN block (gate and
+            # up then form the input of down); the buffers are reused across blocks
+            yn = {(name, n): torch.empty((m, n), dtype=tdt, device=dev) for name, n, _ in synth.GEMMA9B_FFN}
+            calls = [mq.Call(x=xk[k], packed=pk, r=r, rule="prefix", group=GROUP, scales=s_, zeros=z_,
+                             out=yn[(name, n)])
                      for (blk, name, n, k, r, pk, s_, z_) in blocks]
             mq.linear_mixed(calls)
             torch.cuda.synchronize()
