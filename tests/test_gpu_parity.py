@@ -277,6 +277,25 @@ def test_llama_ffn_skinny(mq, llama_ffn, m):
             check_y(y, lay, x, r, O.PREFIX, rows=sample_rows(lay.n, 24))
 
 
+@pytest.mark.parametrize("r", [2, 3, 6])
+def test_llama_ffn_decode_m1_round_rule(mq, llama_ffn, r):
+    # the rounded slice at the full decode shapes (it reads one more plane)
+    for name, lay, pk, s, z in llama_ffn:
+        x = synth.activations(synth.rng_for(2, 20 + r), 1, lay.k, "f16")
+        y = mq.linear(x.to(DEV), pk, r, O.ROUND, 128, s, z)
+        check_y(y, lay, x, r, O.ROUND, rows=sample_rows(lay.n))
+
+
+@pytest.mark.parametrize("m", [1, 8, 40])
+def test_llama_ffn_bf16_decode(mq, llama_ffn, m):
+    # bf16 activations at the full shapes: GEMV at m = 1, skinny above
+    for r in (2, 4, 8):
+        for name, lay, pk, s, z in llama_ffn:
+            x = synth.activations(synth.rng_for(3, 100 + m, r), m, lay.k, "bf16")
+            y = mq.linear(x.to(DEV), pk, r, O.PREFIX, 128, s, z)
+            check_y(y, lay, x, r, O.PREFIX, rows=sample_rows(lay.n, 24))
+
+
 @pytest.mark.parametrize("r", [2, 4, 8])
 def test_llama_ffn_prefill_2048(mq, llama_ffn, r):
     for name, lay, pk, s, z in llama_ffn:
