@@ -50,6 +50,7 @@ struct SkinnyPlan {
   int splits;            // k ranges (1 = no workspace)
   int rounds_per_split;  // 256-wide k rounds per range
   int nt;                // 16-row tiles per wave: 1 (64-row workgroups) or 2 (128-row)
+  int kh;                // teams of 4 waves per workgroup splitting its k range (1 or 2)
 };
 SkinnyPlan plan_skinny(int m, int n, int k);
 size_t skinny_workspace_bytes(int m, int n, int k);

@@ -135,6 +135,9 @@ SHAPES = [
     (12, 384, 3584, 128, "f16"),    # skinny: fourteen rounds split seven ways
     (5, 14400, 512, 64, "f16"),     # skinny with 64-row workgroups (wide n, no k split)
     (20, 14337, 256, 128, "bf16"),  # skinny 64-row workgroups, two m tiles, one-row tail block
+    (20, 14400, 768, 64, "bf16"),   # skinny, two k teams per workgroup: 2 + 1 rounds
+    (33, 14336, 1280, 128, "f16"),  # skinny, two k teams: 3 + 2 rounds, three m tiles
+    (40, 8192, 3840, 128, "f16"),   # skinny, two k teams under a four-way k split (2 + 2, last 2 + 1)
     (65, 300, 768, 64, "bf16"),
     (257, 300, 512, 128, "bf16"),
     (300, 448, 1024, 128, "bf16"),  # prefill tile with split k
