@@ -150,6 +150,19 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Weight planes are streamed: every byte is read once per call, so their
+// loads carry the nontemporal hint, which keeps them from displacing reused
+// data in the caches (measured on plain 4 KB-row streams of 117 and 235 MB:
+// 6.2-6.4 TB/s with the hint against 5.5 without).
+typedef uint32_t stream_u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t stream_u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ stream_u32x4 stream_load16(const uint32_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const stream_u32x4*>(p));
+}
+__device__ __forceinline__ stream_u32x2 stream_load8(const uint32_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const stream_u32x2*>(p));
+}
+
 struct PlanePtrs {
   const uint32_t* p[kPlanes];
 };

@@ -156,13 +156,13 @@ __device__ __forceinline__ void gemv_body(const GemvArgs a, const unsigned blk) 
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
         if (kPlaneBits[p] == 2) {
-          uint4 v = *reinterpret_cast<const uint4*>(a.pl.p[p] + unit * 2);
+          const stream_u32x4 v = stream_load16(a.pl.p[p] + unit * 2);
           rec[buf][i][0][kUnitOff[p]] = v.x;
           rec[buf][i][0][kUnitOff[p] + 1] = v.y;
           rec[buf][i][1][kUnitOff[p]] = v.z;
           rec[buf][i][1][kUnitOff[p] + 1] = v.w;
         } else {
-          uint2 v = *reinterpret_cast<const uint2*>(a.pl.p[p] + unit);
+          const stream_u32x2 v = stream_load8(a.pl.p[p] + unit);
           rec[buf][i][0][kUnitOff[p]] = v.x;
           rec[buf][i][1][kUnitOff[p]] = v.y;
         }
