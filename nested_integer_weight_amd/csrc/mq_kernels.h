@@ -51,8 +51,9 @@ struct SkinnyPlan {
   int rounds_per_split;  // 256-wide k rounds per range
   int nt;                // 16-row tiles per wave: 1 (64-row workgroups) or 2 (128-row)
   int kh;                // teams of 4 waves per workgroup splitting its k range (1 or 2)
+  int run;               // 64-code runs per lane, row and round (1 or 2)
 };
-SkinnyPlan plan_skinny(int m, int n, int k);
+SkinnyPlan plan_skinny(int m, int n, int k, int group, int planes);
 size_t skinny_workspace_bytes(int m, int n, int k);
 hipError_t launch_skinny(const LinearArgs& a, void* workspace, size_t workspace_bytes, hipStream_t s);
 

@@ -53,7 +53,7 @@ constexpr int kWaves = 4;
 // NT = 1 (64 rows, for wide n: enough workgroups without splitting k)
 template <int NT>
 constexpr int cols_per_block() { return 16 * NT * kWaves; }
-constexpr int kRound = 256;                   // k per round
+constexpr int kRound = 256;                   // k per round at one chunk per lane
 
 struct SkinnyArgs {
   const uint16_t* x;
@@ -87,11 +87,17 @@ __device__ __forceinline__ uint32_t dq_f16x2(uint32_t magic_pair, f16x2 c, f16x2
   return __builtin_bit_cast(uint32_t, v);
 }
 
-template <int R, int ROUND, int BF16, int MT, int NT>
+// RUN = 64-code runs per lane, row and round: a round covers RUN * 256 codes,
+// i.e. RUN * 64 bytes of every 2-bit plane row.  RUN = 2 reads whole 128-byte
+// lines per row and round.
+template <int R, int ROUND, int BF16, int MT, int NT, int RUN>
 struct SkinnyWave {
   static constexpr int NP = planes_needed(R, ROUND);
   static constexpr float kDelta = ROUND ? 0.0f : prefix_delta(R);
-  static constexpr int XPIECES = 2 * MT;  // 16-byte X pieces per thread per round
+  static constexpr int KR = kRound * RUN;     // codes per round
+  static constexpr int KS = 8 * RUN;          // MFMA k-steps per round
+  static constexpr int CPR = KR / 8;          // 16-byte X chunks per activation row and round
+  static constexpr int XPIECES = 2 * MT * RUN;  // 16-byte X pieces per thread per round
 
   // weight slots in flight: rounds with few planes carry little data, so they
   // are loaded two rounds ahead; wider ones one round ahead
@@ -104,7 +110,7 @@ struct SkinnyWave {
   size_t upr;
   int gpr;
   // weights of one round per slot: [slot][tile][unit][word]
-  uint32_t rec[kSlots][NT][2][kUnitWords];
+  uint32_t rec[kSlots][NT][2 * RUN][kUnitWords];
   // raw fp16 bits of scale and zero, zero-extended by the load itself (no
   // arithmetic before use, so the loads stay in flight)
   uint32_t sraw[kSlots][NT], zraw[kSlots][NT];
@@ -124,29 +130,31 @@ struct SkinnyWave {
       for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // X piece p = tid + 256 j is 16-byte chunk q = p % 32 of row p / 32 of the
-  // round: 32 consecutive lanes read one row's 512 contiguous bytes.  The
-  // chunk holds k = 8 q .. 8 q + 7, i.e. k-step q % 8 of lane group q / 8, so
-  // it goes to LDS block (m tile, k step) = (row / 16, q % 8) at fragment
-  // position 16 (q / 8) + row % 16, xor-ed with the k step: the eight
+  // X piece p = tid + 256 j is 16-byte chunk q = p % CPR of row p / CPR of
+  // the round: CPR consecutive lanes read one row's contiguous round slice.
+  // The chunk holds k = 8 q .. 8 q + 7, i.e. k-step i = q % KS of lane group
+  // q / KS, so it goes to LDS block (m tile, k step) = (row / 16, i) at
+  // fragment position 16 (q / KS) + row % 16, xor-ed with i % 8: the eight
   // consecutive lanes that one ds_write_b128 clock serves then hit distinct
-  // banks, and the fragment reads (lane ^ step) stay contiguous per 8 lanes.
-  // Rows past m are clamped; they only feed output rows that are not stored.
+  // banks, and the fragment reads (lane ^ (i % 8)) stay contiguous per 8
+  // lanes.  Rows past m are clamped; they only feed output rows that are not
+  // stored.
   __device__ __forceinline__ void load_x(int rnd) {
-    const int kr = kb0 + rnd * kRound;
+    const int kr = kb0 + rnd * KR;
 #pragma unroll
     for (int j = 0; j < XPIECES; ++j) {
       const int p = tid + 256 * j;
-      const int row = min(p >> 5, a.m - 1);
-      xreg[j] = *reinterpret_cast<const u32x4*>(a.x + (size_t)row * a.k + kr + 8 * (p & 31));
+      const int row = min(p / CPR, a.m - 1);
+      xreg[j] = *reinterpret_cast<const u32x4*>(a.x + (size_t)row * a.k + kr + 8 * (p % CPR));
     }
   }
   __device__ __forceinline__ void store_x(u32x4* xs) {
 #pragma unroll
     for (int j = 0; j < XPIECES; ++j) {
       const int p = tid + 256 * j;
-      const int row = p >> 5, q = p & 31;
-      xs[((row >> 4) * 8 + (q & 7)) * 64 + (((q >> 3) * 16 + (row & 15)) ^ (q & 7))] = xreg[j];
+      const int row = p / CPR, q = p % CPR;
+      const int i = q % KS;
+      xs[((row >> 4) * KS + i) * 64 + (((q / KS) * 16 + (row & 15)) ^ (i & 7))] = xreg[j];
     }
   }
 
@@ -154,17 +162,28 @@ struct SkinnyWave {
   template <int SLOT, int T>
   __device__ __forceinline__ void load_w_tile(int kc) {
     const int row = min(nw + 16 * T + c, a.n - 1);
-    const size_t u0 = (size_t)row * upr + (size_t)(kc >> 5);  // even: k % 256 == 0
+    // first unit of the chunk: a multiple of 2 RUN (k % KR == 0), so the
+    // vector loads below are aligned to their size
+    const size_t u0 = (size_t)row * upr + (size_t)(kc >> 5);
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       if (kPlaneBits[p] == 2) {
-        const u32x4 v = reinterpret_cast<const u32x4*>(a.pl.p[p])[u0 >> 1];
+#pragma unroll
+        for (int h = 0; h < RUN; ++h) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(a.pl.p[p] + 2 * (u0 + 2 * h));
+          rec[SLOT][T][2 * h][kUnitOff[p]] = v.x;
+          rec[SLOT][T][2 * h][kUnitOff[p] + 1] = v.y;
+          rec[SLOT][T][2 * h + 1][kUnitOff[p]] = v.z;
+          rec[SLOT][T][2 * h + 1][kUnitOff[p] + 1] = v.w;
+        }
+      } else if constexpr (RUN == 2) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(a.pl.p[p] + u0);
         rec[SLOT][T][0][kUnitOff[p]] = v.x;
-        rec[SLOT][T][0][kUnitOff[p] + 1] = v.y;
-        rec[SLOT][T][1][kUnitOff[p]] = v.z;
-        rec[SLOT][T][1][kUnitOff[p] + 1] = v.w;
+        rec[SLOT][T][1][kUnitOff[p]] = v.y;
+        rec[SLOT][T][2][kUnitOff[p]] = v.z;
+        rec[SLOT][T][3][kUnitOff[p]] = v.w;
       } else {
-        const u32x2 v = reinterpret_cast<const u32x2*>(a.pl.p[p])[u0 >> 1];
+        const u32x2 v = *reinterpret_cast<const u32x2*>(a.pl.p[p] + u0);
         rec[SLOT][T][0][kUnitOff[p]] = v.x;
         rec[SLOT][T][1][kUnitOff[p]] = v.y;
       }
@@ -175,12 +194,13 @@ struct SkinnyWave {
   }
   template <int SLOT>
   __device__ __forceinline__ void load_w(int rnd) {
-    const int kc = kb0 + rnd * kRound + 64 * g;  // first code of this lane's chunk
+    const int kc = kb0 + rnd * KR + 64 * RUN * g;  // first code of this lane's chunk
     load_w_tile<SLOT, 0>(kc);
     if constexpr (NT == 2) load_w_tile<SLOT, 1>(kc);
   }
 
   // weight operand of MFMA k-step I for row tile T: codes [8 I, 8 I + 8) of the chunk
+  // (a chunk of 64 RUN codes lies in one quantization group: group % (64 RUN) == 0)
   // (every array index here is a compile-time constant, so the staging arrays
   // stay in registers)
   template <int SLOT, int I, int T>
@@ -219,7 +239,7 @@ struct SkinnyWave {
       const u32x4 wf1 = w_frag<SLOT, I, NT - 1>();
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const u32x4 xf = xs[(mt * 8 + I) * 64 + (lane ^ I)];
+        const u32x4 xf = xs[(mt * KS + I) * 64 + (lane ^ (I & 7))];
         acc[mt][0] = mfma<BF16>(xf, wf0, acc[mt][0]);
         acc[mt][NT - 1] = mfma<BF16>(xf, wf1, acc[mt][NT - 1]);
       }
@@ -227,22 +247,18 @@ struct SkinnyWave {
       const u32x4 wf0 = w_frag<SLOT, I, 0>();
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const u32x4 xf = xs[(mt * 8 + I) * 64 + (lane ^ I)];
+        const u32x4 xf = xs[(mt * KS + I) * 64 + (lane ^ (I & 7))];
         acc[mt][0] = mfma<BF16>(xf, wf0, acc[mt][0]);
       }
     }
   }
 
-  template <int SLOT>
+  template <int SLOT, int I = 0>
   __device__ __forceinline__ void compute(const u32x4* xs) {
-    kstep<SLOT, 0>(xs);
-    kstep<SLOT, 1>(xs);
-    kstep<SLOT, 2>(xs);
-    kstep<SLOT, 3>(xs);
-    kstep<SLOT, 4>(xs);
-    kstep<SLOT, 5>(xs);
-    kstep<SLOT, 6>(xs);
-    kstep<SLOT, 7>(xs);
+    if constexpr (I < KS) {
+      kstep<SLOT, I>(xs);
+      compute<SLOT, I + 1>(xs);
+    }
   }
 
   // Round rnd computes from slot SLOT and LDS buffer rnd & 1.  It first issues
@@ -296,17 +312,18 @@ struct SkinnyWave {
 // weight bytes are in flight per CU.
 // Two waves per SIMD is enough to cover the latency with the prefetch above;
 // asking for more would make the compiler spill the staging registers.
-template <int R, int ROUND, int BF16, int MT, int NT, int KH>
+template <int R, int ROUND, int BF16, int MT, int NT, int KH, int RUN>
 __global__ __launch_bounds__(256 * KH) __attribute__((amdgpu_waves_per_eu(2, 2))) void skinny_kernel(SkinnyArgs a) {
-  __shared__ u32x4 Xs[KH][2][MT * 8 * 64];
+  constexpr int KR = kRound * RUN;
+  __shared__ u32x4 Xs[KH][2][MT * 8 * RUN * 64];
   const int team = KH == 2 ? (int)(threadIdx.x >> 8) : 0;
   const int tid = threadIdx.x & 255;
   const int n0 = blockIdx.x * cols_per_block<NT>();
-  const int ks = blockIdx.y * a.rounds_per_split * kRound;
-  const int nr_all = min(a.rounds_per_split, (a.k - ks) / kRound);
+  const int ks = blockIdx.y * a.rounds_per_split * KR;
+  const int nr_all = min(a.rounds_per_split, (a.k - ks) / KR);
   const int nr0 = (nr_all + KH - 1) / KH;
   const int nr = team == 0 ? nr0 : nr_all - nr0;
-  SkinnyWave<R, ROUND, BF16, MT, NT> w(a, tid, n0, ks + team * nr0 * kRound);
+  SkinnyWave<R, ROUND, BF16, MT, NT, RUN> w(a, tid, n0, ks + team * nr0 * KR);
   if (nr > 0) w.run(nr, Xs[team][0], Xs[team][1]);
   const int lane = tid & 63;
   if constexpr (KH == 2) {
@@ -362,41 +379,63 @@ constexpr int kTargetBlocks = 224;
 
 int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 
-template <int R, int ROUND, int BF16, int NT, int KH>
-hipError_t launch_t(const SkinnyArgs& sa, int mt, dim3 grid, hipStream_t s) {
-  const dim3 block(256 * KH);
-  switch (mt) {
-    case 1:
-      // one m tile runs with one team only (the plan never asks for two)
-      if constexpr (KH == 1) hipLaunchKernelGGL((skinny_kernel<R, ROUND, BF16, 1, NT, 1>), grid, block, 0, s, sa);
-      else return hipErrorInvalidValue;
-      break;
-    case 2: hipLaunchKernelGGL((skinny_kernel<R, ROUND, BF16, 2, NT, KH>), grid, block, 0, s, sa); break;
-    case 3: hipLaunchKernelGGL((skinny_kernel<R, ROUND, BF16, 3, NT, KH>), grid, block, 0, s, sa); break;
-    default: hipLaunchKernelGGL((skinny_kernel<R, ROUND, BF16, 4, NT, KH>), grid, block, 0, s, sa); break;
+// workgroup shapes that are instantiated: two teams need two m tiles, long
+// runs are planned for at most two m tiles, and the X buffers (KH teams x 2
+// rounds x MT tiles x KS steps x 1 KB) fit in 128 KB
+template <int MT, int KH, int RUN>
+constexpr bool shape_ok() { return !(MT == 1 && KH == 2) && (RUN == 1 || MT <= 2) && KH * MT * RUN <= 8; }
+
+template <int R, int ROUND, int BF16, int MT, int NT, int KH, int RUN>
+hipError_t launch_k(const SkinnyArgs& sa, dim3 grid, hipStream_t s) {
+  if constexpr (shape_ok<MT, KH, RUN>()) {
+    hipLaunchKernelGGL((skinny_kernel<R, ROUND, BF16, MT, NT, KH, RUN>), grid, dim3(256 * KH), 0, s, sa);
+    return hipGetLastError();
+  } else {
+    return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
+template <int R, int ROUND, int BF16, int NT, int KH, int RUN>
+hipError_t launch_t(const SkinnyArgs& sa, int mt, dim3 grid, hipStream_t s) {
+  switch (mt) {
+    case 1: return launch_k<R, ROUND, BF16, 1, NT, KH, RUN>(sa, grid, s);
+    case 2: return launch_k<R, ROUND, BF16, 2, NT, KH, RUN>(sa, grid, s);
+    case 3: return launch_k<R, ROUND, BF16, 3, NT, KH, RUN>(sa, grid, s);
+    default: return launch_k<R, ROUND, BF16, 4, NT, KH, RUN>(sa, grid, s);
+  }
+}
+
+// 128-row workgroups (NT = 2) always take one run per round
 template <int R, int ROUND, int BF16>
-hipError_t launch_b(const SkinnyArgs& sa, int mt, int nt, int kh, dim3 grid, hipStream_t s) {
-  if (kh == 2) return nt == 1 ? launch_t<R, ROUND, BF16, 1, 2>(sa, mt, grid, s) : launch_t<R, ROUND, BF16, 2, 2>(sa, mt, grid, s);
-  return nt == 1 ? launch_t<R, ROUND, BF16, 1, 1>(sa, mt, grid, s) : launch_t<R, ROUND, BF16, 2, 1>(sa, mt, grid, s);
+hipError_t launch_b(const SkinnyArgs& sa, int mt, const SkinnyPlan& p, dim3 grid, hipStream_t s) {
+  if (p.nt == 2) return p.kh == 2 ? launch_t<R, ROUND, BF16, 2, 2, 1>(sa, mt, grid, s)
+                                  : launch_t<R, ROUND, BF16, 2, 1, 1>(sa, mt, grid, s);
+  if (p.run == 2) return p.kh == 2 ? launch_t<R, ROUND, BF16, 1, 2, 2>(sa, mt, grid, s)
+                                   : launch_t<R, ROUND, BF16, 1, 1, 2>(sa, mt, grid, s);
+  return p.kh == 2 ? launch_t<R, ROUND, BF16, 1, 2, 1>(sa, mt, grid, s)
+                   : launch_t<R, ROUND, BF16, 1, 1, 1>(sa, mt, grid, s);
 }
 
 template <int R, int ROUND>
-hipError_t launch_d(const SkinnyArgs& sa, int bf16, int mt, int nt, int kh, dim3 grid, hipStream_t s) {
-  return bf16 ? launch_b<R, ROUND, 1>(sa, mt, nt, kh, grid, s) : launch_b<R, ROUND, 0>(sa, mt, nt, kh, grid, s);
+hipError_t launch_d(const SkinnyArgs& sa, int bf16, int mt, const SkinnyPlan& p, dim3 grid, hipStream_t s) {
+  return bf16 ? launch_b<R, ROUND, 1>(sa, mt, p, grid, s) : launch_b<R, ROUND, 0>(sa, mt, p, grid, s);
 }
 
 }  // namespace
 
-SkinnyPlan plan_skinny(int m, int n, int k) {
+SkinnyPlan plan_skinny(int m, int n, int k, int group, int planes) {
   SkinnyPlan p;
-  const int rounds = k / kRound;
   // 64-row workgroups when they alone give the target count (no split-k and
   // no reduction launch); otherwise 128-row workgroups with k split
   p.nt = cdiv(n, cols_per_block<1>()) >= kTargetBlocks ? 1 : 2;
+  // 64-row workgroups read 128-code runs per lane when the groups and k allow
+  // it: 9-16% faster at one m tile; at two m tiles only from three planes up
+  // (r = 2 and 3 lose up to 5%); at three and four m tiles the X buffers of
+  // two teams no longer fit next to the longer rounds, and one team with
+  // long runs is slower than two with short ones
+  const int mt = cdiv(m, 16);
+  p.run = (p.nt == 1 && group % 128 == 0 && k % (2 * kRound) == 0 && (mt == 1 || (mt == 2 && planes >= 3))) ? 2 : 1;
+  const int rounds = k / (kRound * p.run);
   const int blocks_n = p.nt == 1 ? cdiv(n, cols_per_block<1>()) : cdiv(n, cols_per_block<2>());
   int s = cdiv(kTargetBlocks, blocks_n);
   if (s > rounds) s = rounds;
@@ -404,22 +443,25 @@ SkinnyPlan plan_skinny(int m, int n, int k) {
   p.rounds_per_split = cdiv(rounds, s);
   p.splits = cdiv(rounds, p.rounds_per_split);
   // two teams per workgroup from two m tiles up: measured 4-8% faster at
-  // m = 32 and 64; at one m tile neither form wins consistently
-  p.kh = m > 16 ? 2 : 1;
+  // m = 32 and 64; at one m tile neither form wins consistently.  Their X
+  // buffers must fit in 128 KB of LDS.
+  p.kh = (m > 16 && 2 * mt * p.run <= 8) ? 2 : 1;
   return p;
 }
 
 size_t skinny_workspace_bytes(int m, int n, int k) {
   if (!skinny_eligible(m, k)) return 0;
-  const SkinnyPlan p = plan_skinny(m, n, k);
+  // the k split does not depend on the group: runs of 128 codes are only
+  // used by 64-row workgroups, which never split k
+  const SkinnyPlan p = plan_skinny(m, n, k, 128, 5);
   return p.splits > 1 ? (size_t)p.splits * (size_t)m * (size_t)n * sizeof(float) : 0;
 }
 
 hipError_t launch_skinny(const LinearArgs& la, void* workspace, size_t workspace_bytes, hipStream_t s) {
-  SkinnyPlan p = plan_skinny(la.m, la.n, la.k);
+  SkinnyPlan p = plan_skinny(la.m, la.n, la.k, la.group, planes_needed(la.r, la.round_rule));
   if (p.splits > 1 && workspace_bytes < (size_t)p.splits * (size_t)la.m * (size_t)la.n * sizeof(float)) {
     p.splits = 1;
-    p.rounds_per_split = la.k / kRound;
+    p.rounds_per_split = la.k / (kRound * p.run);
   }
   SkinnyArgs sa;
   sa.x = static_cast<const uint16_t*>(la.x);
@@ -438,8 +480,8 @@ hipError_t launch_skinny(const LinearArgs& la, void* workspace, size_t workspace
   hipError_t e;
 #define MQ_SK_CASE(RR)                                                                               \
   case RR:                                                                                           \
-    e = la.round_rule ? launch_d<RR, 1>(sa, la.bf16, mt, p.nt, p.kh, grid, s)                           \
-                      : launch_d<RR, 0>(sa, la.bf16, mt, p.nt, p.kh, grid, s);                          \
+    e = la.round_rule ? launch_d<RR, 1>(sa, la.bf16, mt, p, grid, s)                           \
+                      : launch_d<RR, 0>(sa, la.bf16, mt, p, grid, s);                          \
     break;
   switch (la.r) {
     MQ_SK_CASE(2)
