@@ -425,16 +425,16 @@ hipError_t launch_d(const SkinnyArgs& sa, int bf16, int mt, const SkinnyPlan& p,
 
 SkinnyPlan plan_skinny(int m, int n, int k, int group, int planes) {
   SkinnyPlan p;
-  // 64-row workgroups when they alone give the target count (no split-k and
-  // no reduction launch); otherwise 128-row workgroups with k split
-  p.nt = cdiv(n, cols_per_block<1>()) >= kTargetBlocks ? 1 : 2;
-  // 64-row workgroups read 128-code runs per lane when the groups and k allow
-  // it: 9-16% faster at one m tile; at two m tiles only from three planes up
-  // (r = 2 and 3 lose up to 5%); at three and four m tiles the X buffers of
-  // two teams no longer fit next to the longer rounds, and one team with
-  // long runs is slower than two with short ones
+  // 128-code runs per lane when the groups and k allow it: 9-16% faster at
+  // one m tile; at two m tiles only from three planes up (r = 2 and 3 lose
+  // up to 5%); at three and four m tiles the X buffers of two teams no longer
+  // fit next to the longer rounds, and one team with long runs is slower
+  // than two with short ones.  Long runs go with 64-row workgroups.
   const int mt = cdiv(m, 16);
-  p.run = (p.nt == 1 && group % 128 == 0 && k % (2 * kRound) == 0 && (mt == 1 || (mt == 2 && planes >= 3))) ? 2 : 1;
+  p.run = (group % 128 == 0 && k % (2 * kRound) == 0 && (mt == 1 || (mt == 2 && planes >= 3))) ? 2 : 1;
+  // Otherwise 64-row workgroups when they alone give the target count (no
+  // split-k and no reduction launch), else 128-row workgroups with k split.
+  p.nt = (p.run == 2 || cdiv(n, cols_per_block<1>()) >= kTargetBlocks) ? 1 : 2;
   const int rounds = k / (kRound * p.run);
   const int blocks_n = p.nt == 1 ? cdiv(n, cols_per_block<1>()) : cdiv(n, cols_per_block<2>());
   int s = cdiv(kTargetBlocks, blocks_n);
@@ -451,10 +451,12 @@ SkinnyPlan plan_skinny(int m, int n, int k, int group, int planes) {
 
 size_t skinny_workspace_bytes(int m, int n, int k) {
   if (!skinny_eligible(m, k)) return 0;
-  // the k split does not depend on the group: runs of 128 codes are only
-  // used by 64-row workgroups, which never split k
-  const SkinnyPlan p = plan_skinny(m, n, k, 128, 5);
-  return p.splits > 1 ? (size_t)p.splits * (size_t)m * (size_t)n * sizeof(float) : 0;
+  // the k split depends on the run length, which depends on the group and
+  // the width: size for the larger of the two plans
+  const SkinnyPlan p1 = plan_skinny(m, n, k, 64, 1);
+  const SkinnyPlan p2 = plan_skinny(m, n, k, 128, 5);
+  const int splits = p1.splits > p2.splits ? p1.splits : p2.splits;
+  return splits > 1 ? (size_t)splits * (size_t)m * (size_t)n * sizeof(float) : 0;
 }
 
 hipError_t launch_skinny(const LinearArgs& la, void* workspace, size_t workspace_bytes, hipStream_t s) {
