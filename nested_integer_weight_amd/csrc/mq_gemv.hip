@@ -101,7 +101,11 @@ __device__ __forceinline__ float dot2h(uint32_t a, uint32_t b, float c) {
 // come in with one dword load per lane (quad lane t fetches the two groups of
 // its quad for row t) and DPP quad broadcasts hand every lane its own value;
 // otherwise each row costs two 16-bit loads per lane.
-template <int R, int ROUND, int MT, int BF16, int ROWS, int SZ4>
+// XW = 1: the workgroup's lanes cover one row's slices (several waves when
+// k > 4096) and walk ROWS rows.  XW = 4 (k <= 4096, one wave per row): four
+// waves with ROWS rows each share a workgroup, and the workgroup stages the
+// activations once through LDS instead of every wave reading all of X.
+template <int R, int ROUND, int MT, int BF16, int ROWS, int SZ4, int XW>
 __device__ __forceinline__ void gemv_body(const GemvArgs a, const unsigned blk) {
   constexpr int NP = planes_needed(R, ROUND);
   // width 2, true prefix, fp16: fields go straight from the plane-0 word to
@@ -116,7 +120,7 @@ __device__ __forceinline__ void gemv_body(const GemvArgs a, const unsigned blk) 
   static_assert(NB * RB == ROWS, "row batches");
   constexpr int V = ROWS * MT;
 
-  const int tid = threadIdx.x;
+  const int tid = XW > 1 ? (int)(threadIdx.x & 63) : (int)threadIdx.x;  // lane of the row's slices
   const int lane = tid & 63;
   const int S = a.k >> 6;
   const bool valid = tid < S;            // one lane per 64-code slice; a row spans the workgroup
@@ -124,19 +128,35 @@ __device__ __forceinline__ void gemv_body(const GemvArgs a, const unsigned blk) 
   const size_t upr = (size_t)(a.k >> 5);  // units per row
   const int gpr = a.k / a.group;
   const int gidx = (slice * 64) / a.group;
-  const size_t row0 = (size_t)blk * (size_t)ROWS;
+  const size_t row0 = ((size_t)blk * XW + (XW > 1 ? (threadIdx.x >> 6) : 0)) * (size_t)ROWS;
 
   // ---- 1. issue the activation loads of this slice ----
   // (unconditional loads from clamped addresses; invalid lanes/tokens are
   // zeroed at first use so no load waits behind a branch)
   uint4 xraw[MT][8];
+  constexpr int XC = XW > 1 ? (MT * 512) / (64 * XW) : 1;  // 16-byte X chunks per thread when staged
+  uint4 xst[XC];
+  if constexpr (XW == 1) {
 #pragma unroll
-  for (int mm = 0; mm < MT; ++mm) {
-    const int mc = mm < a.m ? mm : 0;
-    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + (size_t)mc * a.k +
-                                                      (size_t)slice * 64);
+    for (int mm = 0; mm < MT; ++mm) {
+      const int mc = mm < a.m ? mm : 0;
+      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + (size_t)mc * a.k +
+                                                        (size_t)slice * 64);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) xraw[mm][i] = src[i];
+      for (int i = 0; i < 8; ++i) xraw[mm][i] = src[i];
+    }
+  } else {
+    // chunk c = (token mm, slice sl, piece i) with consecutive threads on
+    // consecutive 16-byte pieces of X; clamped reads for idle slices/tokens
+#pragma unroll
+    for (int j = 0; j < XC; ++j) {
+      const int c = (int)threadIdx.x + 64 * XW * j;
+      const int mm = c >> 9, sl = (c >> 3) & 63, i = c & 7;
+      const int mc = mm < a.m ? mm : 0;
+      const int sc = sl < S ? sl : 0;
+      xst[j] = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + (size_t)mc * a.k +
+                                              (size_t)sc * 64)[i];
+    }
   }
 
   // ---- 2. issue the plane loads of the first row batch ----
@@ -182,6 +202,21 @@ __device__ __forceinline__ void gemv_body(const GemvArgs a, const unsigned blk) 
       sq[q] = *reinterpret_cast<const uint32_t*>(a.scales + row * gpr + qgrp_c);
       zq[q] = *reinterpret_cast<const uint32_t*>(a.zeros + row * gpr + qgrp_c);
     }
+  }
+  if constexpr (XW > 1) {
+    // [token][piece][slice]: a wave's reads of one piece are 64 consecutive
+    // 16-byte entries
+    __shared__ uint4 xlds[MT * 8 * 64];
+#pragma unroll
+    for (int j = 0; j < XC; ++j) {
+      const int c = (int)threadIdx.x + 64 * XW * j;
+      xlds[((c >> 9) * 8 + (c & 7)) * 64 + ((c >> 3) & 63)] = xst[j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int mm = 0; mm < MT; ++mm)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) xraw[mm][i] = xlds[(mm * 8 + i) * 64 + lane];
   }
 
   // ---- 3. activations: register layout, slice sums ----
@@ -374,7 +409,7 @@ __device__ __forceinline__ void gemv_body(const GemvArgs a, const unsigned blk) 
   };
 
   const int nwaves = blockDim.x >> 6;
-  if (nwaves == 1) {
+  if (XW > 1 || nwaves == 1) {
     if (holder) store(idx, acc[0]);
   } else {
     // a row spans several waves: combine the per-wave sums through LDS
@@ -390,9 +425,9 @@ __device__ __forceinline__ void gemv_body(const GemvArgs a, const unsigned blk) 
   }
 }
 
-template <int R, int ROUND, int MT, int BF16, int ROWS, int SZ4>
+template <int R, int ROUND, int MT, int BF16, int ROWS, int SZ4, int XW>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
-  gemv_body<R, ROUND, MT, BF16, ROWS, SZ4>(a, blockIdx.x);
+  gemv_body<R, ROUND, MT, BF16, ROWS, SZ4, XW>(a, blockIdx.x);
 }
 
 // Several independent calls of one shape class (same m, k, width, rule,
@@ -405,18 +440,29 @@ struct GemvBatch {
   int ncalls;
 };
 
-template <int R, int ROUND, int MT, int BF16, int ROWS, int SZ4>
+template <int R, int ROUND, int MT, int BF16, int ROWS, int SZ4, int XW>
 __global__ __launch_bounds__(256) void gemv_batch_kernel(GemvBatch b) {
   int c = 0;
 #pragma unroll
   for (int i = 1; i < kGemvMaxBatch; ++i)
     if (i < b.ncalls && (int)blockIdx.x >= b.first_block[i]) c = i;
-  gemv_body<R, ROUND, MT, BF16, ROWS, SZ4>(b.call[c], blockIdx.x - (unsigned)b.first_block[c]);
+  gemv_body<R, ROUND, MT, BF16, ROWS, SZ4, XW>(b.call[c], blockIdx.x - (unsigned)b.first_block[c]);
+}
+
+template <int R, int ROUND, int MT, int BF16, int SZ4, int XW, int ROWS>
+static void gemv_launch_k(const GemvBatch& b, int ncalls, unsigned blocks, int threads, size_t lds, hipStream_t s) {
+  if (ncalls == 1)
+    hipLaunchKernelGGL((gemv_kernel<R, ROUND, MT, BF16, ROWS, SZ4, XW>), dim3(blocks), dim3(threads), lds, s, b.call[0]);
+  else
+    hipLaunchKernelGGL((gemv_batch_kernel<R, ROUND, MT, BF16, ROWS, SZ4, XW>), dim3(blocks), dim3(threads), lds, s, b);
 }
 
 template <int R, int ROUND, int MT, int BF16>
 static hipError_t gemv_launch_t(const LinearArgs* la, int ncalls, hipStream_t s) {
   constexpr int ROWS = (MT >= 4) ? 4 : 8;
+  // every call of a batch shares k and group, hence the workgroup shape
+  const int S = la[0].k / 64;
+  const int xw = S <= 64 ? 4 : 1;  // four row groups share the staged X when a row fits one wave
   GemvBatch b;
   unsigned blocks = 0;
   for (int i = 0; i < ncalls; ++i) {
@@ -431,29 +477,23 @@ static hipError_t gemv_launch_t(const LinearArgs* la, int ncalls, hipStream_t s)
     a.k = la[i].k;
     a.group = la[i].group;
     b.first_block[i] = (int)blocks;
-    blocks += (unsigned)((la[i].n + ROWS - 1) / ROWS);
+    blocks += (unsigned)((la[i].n + xw * ROWS - 1) / (xw * ROWS));
   }
   for (int i = ncalls; i < kGemvMaxBatch; ++i) {
     b.call[i] = b.call[0];
     b.first_block[i] = (int)blocks;
   }
   b.ncalls = ncalls;
-  // every call of a batch shares k and group, hence the workgroup shape
-  const int S = la[0].k / 64;
-  const int threads = ((S + 63) / 64) * 64;  // one lane per 64-code slice, whole waves
-  const size_t lds = (threads > 64) ? (size_t)(threads / 64) * ROWS * MT * sizeof(float) : 0;
   const int gpr = la[0].k / la[0].group;
   const bool sz4 = la[0].group == 128 && gpr % 2 == 0;
-  if (ncalls == 1) {
-    if (sz4)
-      hipLaunchKernelGGL((gemv_kernel<R, ROUND, MT, BF16, ROWS, 1>), dim3(blocks), dim3(threads), lds, s, b.call[0]);
-    else
-      hipLaunchKernelGGL((gemv_kernel<R, ROUND, MT, BF16, ROWS, 0>), dim3(blocks), dim3(threads), lds, s, b.call[0]);
+  if (xw == 4) {
+    if (sz4) gemv_launch_k<R, ROUND, MT, BF16, 1, 4, ROWS>(b, ncalls, blocks, 256, 0, s);
+    else gemv_launch_k<R, ROUND, MT, BF16, 0, 4, ROWS>(b, ncalls, blocks, 256, 0, s);
   } else {
-    if (sz4)
-      hipLaunchKernelGGL((gemv_batch_kernel<R, ROUND, MT, BF16, ROWS, 1>), dim3(blocks), dim3(threads), lds, s, b);
-    else
-      hipLaunchKernelGGL((gemv_batch_kernel<R, ROUND, MT, BF16, ROWS, 0>), dim3(blocks), dim3(threads), lds, s, b);
+    const int threads = ((S + 63) / 64) * 64;  // one lane per 64-code slice, whole waves
+    const size_t lds = (size_t)(threads / 64) * ROWS * MT * sizeof(float);
+    if (sz4) gemv_launch_k<R, ROUND, MT, BF16, 1, 1, ROWS>(b, ncalls, blocks, threads, lds, s);
+    else gemv_launch_k<R, ROUND, MT, BF16, 0, 1, ROWS>(b, ncalls, blocks, threads, lds, s);
   }
   return hipGetLastError();
 }
