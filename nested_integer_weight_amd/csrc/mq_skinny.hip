@@ -90,7 +90,10 @@ __device__ __forceinline__ uint32_t dq_f16x2(uint32_t magic_pair, f16x2 c, f16x2
 // RUN = 64-code runs per lane, row and round: a round covers RUN * 256 codes,
 // i.e. RUN * 64 bytes of every 2-bit plane row.  RUN = 2 reads whole 128-byte
 // lines per row and round.
-template <int R, int ROUND, int BF16, int MT, int NT, int RUN>
+// XB = X buffers per team: 2 (the next round's X is staged while the current
+// one is read) or 1 (staged after a barrier that follows the reads, when two
+// buffers of long rounds would not fit in LDS)
+template <int R, int ROUND, int BF16, int MT, int NT, int RUN, int XB>
 struct SkinnyWave {
   static constexpr int NP = planes_needed(R, ROUND);
   static constexpr float kDelta = ROUND ? 0.0f : prefix_delta(R);
@@ -273,7 +276,12 @@ struct SkinnyWave {
     __builtin_amdgcn_sched_barrier(0);
     load_w<(SLOT + kSlots - 1) % kSlots>(min(rnd + kSlots - 1, last));
     compute<SLOT>((rnd & 1) ? xs1 : xs0);
-    store_x((rnd & 1) ? xs0 : xs1);
+    if constexpr (XB == 1) {
+      __syncthreads();
+      store_x(xs0);
+    } else {
+      store_x((rnd & 1) ? xs0 : xs1);
+    }
     __syncthreads();
   }
 
@@ -304,6 +312,11 @@ struct SkinnyWave {
   }
 };
 
+// two X buffers per team unless two teams with long rounds at three or four
+// m tiles need one each to stay within 128 KB of LDS
+template <int MT, int KH, int RUN>
+constexpr int x_buffers() { return (KH == 2 && RUN == 2 && MT >= 3) ? 1 : 2; }
+
 // KH teams of 4 waves share a workgroup and split its k range: team 0 takes
 // the first ceil(nr / KH) rounds, team 1 the rest, each with its own X
 // buffers, and team 1 hands its partial tiles to team 0 through LDS at the
@@ -315,7 +328,8 @@ struct SkinnyWave {
 template <int R, int ROUND, int BF16, int MT, int NT, int KH, int RUN>
 __global__ __launch_bounds__(256 * KH) __attribute__((amdgpu_waves_per_eu(2, 2))) void skinny_kernel(SkinnyArgs a) {
   constexpr int KR = kRound * RUN;
-  __shared__ u32x4 Xs[KH][2][MT * 8 * RUN * 64];
+  constexpr int XB = x_buffers<MT, KH, RUN>();
+  __shared__ u32x4 Xs[KH][XB][MT * 8 * RUN * 64];
   const int team = KH == 2 ? (int)(threadIdx.x >> 8) : 0;
   const int tid = threadIdx.x & 255;
   const int n0 = blockIdx.x * cols_per_block<NT>();
@@ -323,14 +337,15 @@ __global__ __launch_bounds__(256 * KH) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int nr_all = min(a.rounds_per_split, (a.k - ks) / KR);
   const int nr0 = (nr_all + KH - 1) / KH;
   const int nr = team == 0 ? nr0 : nr_all - nr0;
-  SkinnyWave<R, ROUND, BF16, MT, NT, RUN> w(a, tid, n0, ks + team * nr0 * KR);
-  if (nr > 0) w.run(nr, Xs[team][0], Xs[team][1]);
+  SkinnyWave<R, ROUND, BF16, MT, NT, RUN, XB> w(a, tid, n0, ks + team * nr0 * KR);
+  if (nr > 0) w.run(nr, Xs[team][0], Xs[team][XB - 1]);
   const int lane = tid & 63;
   if constexpr (KH == 2) {
-    // run() passes nr + 1 barriers (none for nr = 0); team 1, which may have
-    // one round fewer, passes the missing ones here so that the two teams'
-    // barriers pair up
-    const int pad = (nr0 > 0 ? nr0 + 1 : 0) - (nr > 0 ? nr + 1 : 0);
+    // run() passes 1 + (3 - XB) nr barriers (none for nr = 0); team 1, which
+    // may have one round fewer, passes the missing ones here so that the two
+    // teams' barriers pair up
+    constexpr int BPR = 3 - XB;  // barriers per round
+    const int pad = (nr0 > 0 ? 1 + BPR * nr0 : 0) - (nr > 0 ? 1 + BPR * nr : 0);
     for (int i = 0; i < pad; ++i) __syncthreads();
     // every wave is past its last round: team 1's X buffers are free
     f32x4* part = reinterpret_cast<f32x4*>(&Xs[1][0][0]);
@@ -380,10 +395,13 @@ constexpr int kTargetBlocks = 224;
 int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 
 // workgroup shapes that are instantiated: two teams need two m tiles, long
-// runs are planned for at most two m tiles, and the X buffers (KH teams x 2
-// rounds x MT tiles x KS steps x 1 KB) fit in 128 KB
+// runs at three or four m tiles come with two teams, and the X buffers
+// (KH teams x XB x MT tiles x KS steps x 1 KB) fit in 128 KB
 template <int MT, int KH, int RUN>
-constexpr bool shape_ok() { return !(MT == 1 && KH == 2) && (RUN == 1 || MT <= 2) && KH * MT * RUN <= 8; }
+constexpr bool shape_ok() {
+  return !(MT == 1 && KH == 2) && (RUN == 1 || MT <= 2 || (MT == 3 && KH == 2)) &&
+         KH * x_buffers<MT, KH, RUN>() * MT * RUN <= 16;
+}
 
 template <int R, int ROUND, int BF16, int MT, int NT, int KH, int RUN>
 hipError_t launch_k(const SkinnyArgs& sa, dim3 grid, hipStream_t s) {
@@ -426,12 +444,12 @@ hipError_t launch_d(const SkinnyArgs& sa, int bf16, int mt, const SkinnyPlan& p,
 SkinnyPlan plan_skinny(int m, int n, int k, int group, int planes) {
   SkinnyPlan p;
   // 128-code runs per lane when the groups and k allow it: 9-16% faster at
-  // one m tile; at two m tiles only from three planes up (r = 2 and 3 lose
-  // up to 5%); at three and four m tiles the X buffers of two teams no longer
-  // fit next to the longer rounds, and one team with long runs is slower
-  // than two with short ones.  Long runs go with 64-row workgroups.
+  // one m tile; at two and three m tiles only from three planes up (r = 2
+  // and 3 lose up to 8%, r = 8 gains 7-9%); at four m tiles the longer rounds
+  // need more registers than two waves per SIMD leave.  Long runs go with
+  // 64-row workgroups.
   const int mt = cdiv(m, 16);
-  p.run = (group % 128 == 0 && k % (2 * kRound) == 0 && (mt == 1 || (mt == 2 && planes >= 3))) ? 2 : 1;
+  p.run = (group % 128 == 0 && k % (2 * kRound) == 0 && (mt == 1 || (mt <= 3 && planes >= 3))) ? 2 : 1;
   // Otherwise 64-row workgroups when they alone give the target count (no
   // split-k and no reduction launch), else 128-row workgroups with k split.
   p.nt = (p.run == 2 || cdiv(n, cols_per_block<1>()) >= kTargetBlocks) ? 1 : 2;
@@ -443,9 +461,9 @@ SkinnyPlan plan_skinny(int m, int n, int k, int group, int planes) {
   p.rounds_per_split = cdiv(rounds, s);
   p.splits = cdiv(rounds, p.rounds_per_split);
   // two teams per workgroup from two m tiles up: measured 4-8% faster at
-  // m = 32 and 64; at one m tile neither form wins consistently.  Their X
-  // buffers must fit in 128 KB of LDS.
-  p.kh = (m > 16 && 2 * mt * p.run <= 8) ? 2 : 1;
+  // m = 32 and 64; at one m tile neither form wins consistently.  With long
+  // runs at three m tiles each team keeps one X buffer (128 KB of LDS).
+  p.kh = m > 16 ? 2 : 1;
   return p;
 }
 

@@ -141,7 +141,8 @@ SHAPES = [
     (9, 14336, 1024, 128, "f16"),   # skinny, 128-code runs per lane: two rounds of 512
     (24, 14336, 1536, 128, "f16"),  # skinny, 128-code runs (r >= 4), two k teams: 2 + 1 rounds
     (32, 14352, 512, 128, "bf16"),  # skinny, 128-code runs (r >= 4), two k teams: 1 + 0 rounds, ragged n
-    (40, 14401, 2560, 256, "bf16"), # skinny 64-row workgroups, 64-code runs, three m tiles, group 256, ragged n
+    (40, 14401, 2560, 256, "bf16"), # skinny, 128-code runs, three m tiles, one X buffer per team, group 256, ragged n
+    (48, 14336, 1536, 128, "f16"),  # skinny, 128-code runs, three m tiles, one X buffer per team: 2 + 1 rounds
     (65, 300, 768, 64, "bf16"),
     (257, 300, 512, 128, "bf16"),
     (300, 448, 1024, 128, "bf16"),  # prefill tile with split k
