@@ -77,13 +77,20 @@ __device__ __forceinline__ f32x4 mfma(const u32x4& a, const u32x4& b, const f32x
   }
 }
 
-// RNE(s * (v - z + delta)) for two code bytes given as the halves 1024 + v
+// RNE(s * (v - z + delta)) for two code bytes given as the halves 1024 + v.
+// With an integer offset (delta = 0: the rounded slice, and the full-width
+// prefix) c holds -(1024 + z), an integer below 2048 and so exact in half
+// precision, and one exact addition gives v - z; otherwise c = delta - z and
+// the 1024 goes first.
+template <bool INT_OFFSET>
 __device__ __forceinline__ uint32_t dq_f16x2(uint32_t magic_pair, f16x2 c, f16x2 s) {
-  const f16x2 k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
   f16x2 v = __builtin_bit_cast(f16x2, magic_pair);
-  v = v - k1024;  // exact: the code value
-  v = v + c;      // exact: v - z + delta
-  v = v * s;      // the one rounding
+  if constexpr (!INT_OFFSET) {
+    const f16x2 k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+    v = v - k1024;  // exact: the code value
+  }
+  v = v + c;  // exact: v - z + delta
+  v = v * s;  // the one rounding
   return __builtin_bit_cast(uint32_t, v);
 }
 
@@ -223,14 +230,16 @@ struct SkinnyWave {
       return f;
     } else {
       const _Float16 sh = __builtin_bit_cast(_Float16, (uint16_t)sraw[SLOT][T]);
-      const _Float16 ch = (_Float16)(kDelta - h2f((uint16_t)zraw[SLOT][T]));  // exact: |delta - z| <= 255.5
+      constexpr bool kInt = kDelta == 0.0f;
+      // exact: |delta - z| <= 255.5, and 1024 + z <= 1279 for the integer form
+      const _Float16 ch = (_Float16)((kInt ? -1024.0f : kDelta) - h2f((uint16_t)zraw[SLOT][T]));
       const f16x2 s2 = {sh, sh};
       const f16x2 c2 = {ch, ch};
       u32x4 f;
-      f.x = dq_f16x2(__builtin_amdgcn_perm(0x64646464u, w0, 0x04010400u), c2, s2);
-      f.y = dq_f16x2(__builtin_amdgcn_perm(0x64646464u, w0, 0x04030402u), c2, s2);
-      f.z = dq_f16x2(__builtin_amdgcn_perm(0x64646464u, w1, 0x04010400u), c2, s2);
-      f.w = dq_f16x2(__builtin_amdgcn_perm(0x64646464u, w1, 0x04030402u), c2, s2);
+      f.x = dq_f16x2<kInt>(__builtin_amdgcn_perm(0x64646464u, w0, 0x04010400u), c2, s2);
+      f.y = dq_f16x2<kInt>(__builtin_amdgcn_perm(0x64646464u, w0, 0x04030402u), c2, s2);
+      f.z = dq_f16x2<kInt>(__builtin_amdgcn_perm(0x64646464u, w1, 0x04010400u), c2, s2);
+      f.w = dq_f16x2<kInt>(__builtin_amdgcn_perm(0x64646464u, w1, 0x04030402u), c2, s2);
       return f;
     }
   }
