@@ -273,12 +273,12 @@ struct SkinnyWave {
     }
   }
 
-  // Round rnd computes from slot SLOT and LDS buffer rnd & 1.  It first issues
-  // the X loads of round rnd + 1 and then the weight loads of round
-  // rnd + kSlots - 1 (into the slot of round rnd - 1), in that order, so that
-  // staging X at the end of the round waits for the X loads only and the
-  // weights stay in flight across the barrier.  Past the last round the loads
-  // repeat it.
+  // Round rnd computes from slot SLOT and LDS buffer rnd & 1 (the only buffer
+  // when XB = 1).  It first issues the X loads of round rnd + 1 and then the
+  // weight loads of round rnd + kSlots - 1 (into the slot of round rnd - 1),
+  // in that order, so that staging X at the end of the round waits for the X
+  // loads only and the weights stay in flight across the barrier(s).  Past the
+  // last round the loads repeat it.
   template <int SLOT>
   __device__ __forceinline__ void round(int rnd, int last, u32x4* xs0, u32x4* xs1) {
     load_x(min(rnd + 1, last));
