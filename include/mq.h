@@ -16,7 +16,9 @@
  *   MQ_ROUND  -- MatQuant (summary page, section 3.2; MatGPTQ App. A.1):
  *                code = clamp(round(q / 2^(8-r)), 0, 2^r - 1), ties upward
  *                (the (r+1)-th most significant bit decides);
- *                v = code * 2^(8-r).  Reads r+1 bits per weight (r < 8).
+ *                v = code * 2^(8-r).  Needs r+1 bits per weight (r < 8);
+ *                at plane granularity it reads the planes that cover them:
+ *                3, 4, 6 and 8 bits at r = 2, 3, 4 and 6.
  *   MQ_PREFIX -- MatGPTQ true prefix (MatGPTQ App. A.1):
  *                code = q >> (8-r);  v = code * 2^(8-r) + delta_r,
  *                delta_r = (2^(8-r) - 1) / 2 (centre of the cell).
@@ -144,8 +146,11 @@ size_t mq_linear_workspace_bytes(int32_t m, int32_t n, int32_t k);
  * nn.Linear orientation).  `workspace` (device, may be NULL) of
  * `workspace_bytes` lets the dispatcher split k for shapes with few output
  * tiles; with less than mq_linear_workspace_bytes() it does not split.
- * Kernel choice: m <= 4 streams the planes with a register GEMV; larger m runs
- * the MFMA GEMM that dequantizes weight tiles into LDS. */
+ * Kernel choice: fp16 x with m <= 4 and bf16 x with m == 1 (k <= 16384)
+ * stream the planes with a register GEMV; other m in 2..64 with k % 256 == 0
+ * take the skinny MFMA path (weights dequantized straight into MFMA operand
+ * registers); everything else runs the MFMA GEMM that dequantizes weight
+ * tiles into LDS. */
 mq_status mq_linear(const void* x, int32_t x_dtype, int32_t m, const mq_packed* w, int32_t r,
                     int32_t rule, int32_t group, const uint16_t* scales, const uint16_t* zeros,
                     void* y, void* workspace, size_t workspace_bytes, void* stream);

@@ -93,18 +93,27 @@ def pack_parent(codes: torch.Tensor, out: list | None = None) -> Packed:
 
 
 class Workspace:
-    """A per-device cache of split-k workspace memory owned by the caller."""
+    """Split-k workspace memory owned by the caller: one buffer per (device,
+    stream), so calls on different streams never share partial sums.
+
+    A buffer that is too small is replaced by a larger one, but the replaced
+    buffer stays allocated for the lifetime of this object: a HIP graph
+    captured earlier still holds its address and writes to it on replay."""
 
     def __init__(self):
         self._buf = {}
+        self._retired = []
 
     def get(self, nbytes: int, device) -> torch.Tensor | None:
         if nbytes <= 0:
             return None
-        key = torch.device(device)
+        dev = torch.device(device)
+        key = (dev, torch.cuda.current_stream(dev).cuda_stream)
         b = self._buf.get(key)
         if b is None or b.numel() < nbytes:
-            b = torch.empty(nbytes, dtype=torch.uint8, device=device)
+            if b is not None:
+                self._retired.append(b)
+            b = torch.empty(nbytes, dtype=torch.uint8, device=dev)
             self._buf[key] = b
         return b
 

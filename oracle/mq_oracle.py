@@ -160,10 +160,6 @@ def f32_to_bf16_bits(a32: np.ndarray) -> np.ndarray:
     return rounded.astype(np.uint16)
 
 
-def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
-    return (np.asarray(b, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
-
-
 def export_bf16_bits(w64: np.ndarray) -> np.ndarray:
     return f32_to_bf16_bits(export_f32(w64))
 

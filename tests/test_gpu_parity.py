@@ -1,9 +1,12 @@
 """HIP path vs the CPU oracle, through the C ABI.
 
 Sliced codes and dequantized weights must match bit for bit; Y must be within
-max |dY| / (||X[m,:]|| ||w_hat[n,:]||) <= 2e-3 of the fp64 oracle.  Small
-shapes compare every output; the full workload shapes compare sampled output
-rows (the oracle dequantizes only those rows)."""
+max |dY| / (||X[m,:]|| ||w_hat[n,:]||) <= 2e-3 of the fp64 oracle.  Every test
+compares every output element, at the small shapes and at the full workload
+shapes alike.  One-hot activation rows check each kernel's in-register weight
+operand bit for bit: with X[m, k_m] = 1 and zeros elsewhere, the exact result
+is one dequantized weight, so Y[m, :] must equal the oracle's rounded export of
+w_hat[:, k_m]."""
 import numpy as np
 import pytest
 import torch
@@ -32,23 +35,32 @@ def to_dev(lay):
     return q, s, z
 
 
-def sample_rows(n, count=48, seed=0):
-    rng = np.random.default_rng(seed)
-    base = {0, 1, n // 2, n - 1}
-    base.update(rng.choice(n, size=min(count, n), replace=False).tolist())
-    return np.array(sorted(base))
-
-
-def check_y(y_gpu, lay, x_cpu, r, rule, rows=None, tol=TOL):
+def check_y(y_gpu, lay, x_cpu, r, rule, tol=TOL, w64=None):
+    """Every element of y_gpu against the fp64 oracle."""
     x64 = x_cpu.double().numpy()
-    rows = np.arange(lay.n) if rows is None else rows
-    w64 = O.dequant(lay.q[rows], lay.scales[rows], lay.zeros[rows], r, rule, lay.group)
+    if w64 is None:
+        w64 = O.dequant(lay.q, lay.scales, lay.zeros, r, rule, lay.group)
     y_ref = x64 @ w64.T
-    y = y_gpu.float().cpu().numpy().astype(np.float64)[:, rows]
+    y = y_gpu.float().cpu().numpy().astype(np.float64)
+    assert y.shape == y_ref.shape
     assert np.all(np.isfinite(y))
     err = O.normalized_error(y, y_ref, x64, w64)
     assert err <= tol, f"normalized error {err:.3e}"
     return err
+
+
+_W64 = {}
+
+
+def w64_of(key, lay, r, rule):
+    """The oracle's dequantized [n, k] weights, cached for the last three
+    (matrix, width, rule) keys (a full 8B FFN matrix is 470 MB in fp64)."""
+    k = (key, r, rule)
+    if k not in _W64:
+        while len(_W64) >= 3:
+            _W64.pop(next(iter(_W64)))
+        _W64[k] = O.dequant(lay.q, lay.scales, lay.zeros, r, rule, lay.group)
+    return _W64[k]
 
 
 # ---------------------------------------------------------------------------
@@ -151,17 +163,70 @@ SHAPES = [
 ]
 
 
+_SHAPE_CACHE = {}
+
+
+def shape_case(mq, m, n, k, group, dt):
+    """Layer, packed parent and device tensors of one shape, made once and
+    shared by every (width, rule) of that shape."""
+    key = (m, n, k, group, dt)
+    if key not in _SHAPE_CACHE:
+        _SHAPE_CACHE.clear()
+        lay = synth.make_layer(cfg_id=6, tensor_id=n * 7 + m, n=n, k=k, m=m, group=group, x_dtype=dt)
+        q, s, z = to_dev(lay)
+        _SHAPE_CACHE[key] = (lay, mq.pack_parent(q), s, z, lay.x.to(DEV))
+    return _SHAPE_CACHE[key]
+
+
+# every width and both rules on every shape: together the shapes reach every
+# (width, rule, dtype) instantiation of the GEMV, skinny and GEMM kernels
 @pytest.mark.parametrize("rule", RULES)
-@pytest.mark.parametrize("r", [2, 3, 8])
+@pytest.mark.parametrize("r", WIDTHS)
 @pytest.mark.parametrize("m,n,k,group,dt", SHAPES, ids=lambda v: str(v))
 def test_linear_shapes(mq, m, n, k, group, dt, r, rule):
-    lay = synth.make_layer(cfg_id=6, tensor_id=n * 7 + m, n=n, k=k, m=m, group=group, x_dtype=dt)
-    q, s, z = to_dev(lay)
-    pk = mq.pack_parent(q)
-    x = lay.x.to(DEV)
-    y = mq.linear(x, pk, r, rule, group, s, z)
+    lay, pk, s, z, x = shape_case(mq, m, n, k, group, dt)
+    y = mq.linear(x, pk.truncated(r, rule), r, rule, group, s, z)
     assert y.dtype == x.dtype and y.shape == (m, n)
     check_y(y, lay, lay.x, r, rule)
+
+
+# one case per kernel path and operand form (m, n, k, group, dtype)
+ONE_HOT = [
+    (1, 320, 1024, 128, "f16"),    # GEMV, four row groups share staged X
+    (1, 96, 14336, 128, "f16"),    # GEMV, a row spread over four waves
+    (1, 320, 1024, 64, "bf16"),    # bf16 GEMV
+    (3, 320, 1024, 64, "f16"),     # GEMV, three tokens
+    (2, 320, 1024, 128, "bf16"),   # skinny bf16, 128-code runs
+    (8, 320, 1024, 128, "f16"),    # skinny, 128-code runs, split k
+    (16, 14336, 512, 64, "f16"),   # skinny, 64-code runs, 64-row workgroups
+    (40, 320, 1024, 128, "f16"),   # skinny, two teams, three m tiles
+    (40, 320, 1024, 64, "bf16"),   # skinny bf16, two teams, 64-code runs
+    (64, 640, 1024, 128, "f16"),   # skinny, four m tiles, 128-row workgroups
+    (300, 320, 1024, 128, "f16"),  # GEMM, split k
+    (300, 320, 1024, 64, "bf16"),  # GEMM bf16, split k
+    (257, 512, 512, 128, "bf16"),  # GEMM bf16, ragged m
+]
+
+
+@pytest.mark.parametrize("rule", RULES)
+@pytest.mark.parametrize("r", WIDTHS)
+@pytest.mark.parametrize("m,n,k,group,dt", ONE_HOT, ids=lambda v: str(v))
+def test_one_hot_rows_bitexact(mq, m, n, k, group, dt, r, rule):
+    # X[i, k_i] = 1: the fp32 sum holds exactly one product, weight x 1, so the
+    # output is the kernel's weight value rounded once to the output dtype --
+    # which must be the oracle's one rounding of the exact w_hat.
+    lay = synth.make_layer(cfg_id=8, tensor_id=n * 7 + m, n=n, k=k, m=0, group=group)
+    q, s, z = to_dev(lay)
+    pk = mq.pack_parent(q).truncated(r, rule)
+    kpos = (np.arange(m) * 7919 + 5) % k
+    tdt = torch.float16 if dt == "f16" else torch.bfloat16
+    x = torch.zeros((m, k), dtype=tdt)
+    x[np.arange(m), kpos] = 1.0
+    y = mq.linear(x.to(DEV), pk, r, rule, group, s, z)
+    w64 = O.dequant(lay.q, lay.scales, lay.zeros, r, rule, group)
+    want = (O.export_f16(w64).view(np.uint16) if dt == "f16" else O.export_bf16_bits(w64))[:, kpos].T
+    got = y.cpu().view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, want)
 
 
 def test_linear_m0_is_noop(mq, cfg1):
@@ -255,7 +320,7 @@ def test_mixed_dependent_gemv_calls_keep_order(mq):
 
 
 # ---------------------------------------------------------------------------
-# full workload shapes, sampled rows
+# full workload shapes, every output element
 # ---------------------------------------------------------------------------
 @pytest.fixture(scope="module")
 def llama_ffn(mq):
@@ -263,53 +328,60 @@ def llama_ffn(mq):
     for tid, (name, n, k) in enumerate(synth.LLAMA8B_FFN):
         lay = synth.make_layer(cfg_id=2, tensor_id=tid, n=n, k=k, m=0, group=128, outlier_frac=1e-3)
         q, s, z = to_dev(lay)
-        out.append((name, lay, mq.pack_parent(q), s, z))
+        out.append((tid, lay, mq.pack_parent(q), s, z))
     torch.cuda.synchronize()
     return out
 
 
 @pytest.mark.parametrize("r", WIDTHS)
 def test_llama_ffn_decode_m1(mq, llama_ffn, r):
-    for name, lay, pk, s, z in llama_ffn:
+    # decode at M = 1 with only the planes of this width resident
+    for tid, lay, pk, s, z in llama_ffn:
         x = synth.activations(synth.rng_for(2, 10 + r), 1, lay.k, "f16")
         y = mq.linear(x.to(DEV), pk.truncated(r), r, O.PREFIX, 128, s, z)
-        check_y(y, lay, x, r, O.PREFIX, rows=sample_rows(lay.n))
+        check_y(y, lay, x, r, O.PREFIX, w64=w64_of(tid, lay, r, O.PREFIX))
 
 
-@pytest.mark.parametrize("m", [8, 16, 32, 64])
-def test_llama_ffn_skinny(mq, llama_ffn, m):
-    for r in (2, 3, 4, 8):
-        for name, lay, pk, s, z in llama_ffn:
+@pytest.mark.parametrize("r", [2, 3, 4, 8])
+def test_llama_ffn_skinny(mq, llama_ffn, r):
+    for tid, lay, pk, s, z in llama_ffn:
+        w64 = w64_of(tid, lay, r, O.PREFIX)
+        for m in (8, 16, 32, 64):
             x = synth.activations(synth.rng_for(3, m, r), m, lay.k, "f16")
             y = mq.linear(x.to(DEV), pk, r, O.PREFIX, 128, s, z)
-            check_y(y, lay, x, r, O.PREFIX, rows=sample_rows(lay.n, 24))
+            check_y(y, lay, x, r, O.PREFIX, w64=w64)
 
 
-@pytest.mark.parametrize("r", [2, 3, 6])
-def test_llama_ffn_decode_m1_round_rule(mq, llama_ffn, r):
-    # the rounded slice at the full decode shapes (it reads one more plane)
-    for name, lay, pk, s, z in llama_ffn:
-        x = synth.activations(synth.rng_for(2, 20 + r), 1, lay.k, "f16")
-        y = mq.linear(x.to(DEV), pk, r, O.ROUND, 128, s, z)
-        check_y(y, lay, x, r, O.ROUND, rows=sample_rows(lay.n))
+@pytest.mark.parametrize("r", [2, 3, 4, 6])
+def test_llama_ffn_round_rule(mq, llama_ffn, r):
+    # the rounded slice at the full shapes (it reads one more plane), at decode
+    # and at a skinny batch
+    for tid, lay, pk, s, z in llama_ffn:
+        w64 = w64_of(tid, lay, r, O.ROUND)
+        for m in (1, 24):
+            x = synth.activations(synth.rng_for(2, 20 + r, m), m, lay.k, "f16")
+            y = mq.linear(x.to(DEV), pk.truncated(r, O.ROUND), r, O.ROUND, 128, s, z)
+            check_y(y, lay, x, r, O.ROUND, w64=w64)
 
 
-@pytest.mark.parametrize("m", [1, 8, 40])
-def test_llama_ffn_bf16_decode(mq, llama_ffn, m):
+@pytest.mark.parametrize("r", [2, 4, 6, 8])
+def test_llama_ffn_bf16_decode(mq, llama_ffn, r):
     # bf16 activations at the full shapes: GEMV at m = 1, skinny above
-    for r in (2, 4, 8):
-        for name, lay, pk, s, z in llama_ffn:
+    for tid, lay, pk, s, z in llama_ffn:
+        w64 = w64_of(tid, lay, r, O.PREFIX)
+        for m in (1, 8, 40):
             x = synth.activations(synth.rng_for(3, 100 + m, r), m, lay.k, "bf16")
             y = mq.linear(x.to(DEV), pk, r, O.PREFIX, 128, s, z)
-            check_y(y, lay, x, r, O.PREFIX, rows=sample_rows(lay.n, 24))
+            check_y(y, lay, x, r, O.PREFIX, w64=w64)
 
 
 @pytest.mark.parametrize("r", [2, 4, 8])
 def test_llama_ffn_prefill_2048(mq, llama_ffn, r):
-    for name, lay, pk, s, z in llama_ffn:
+    # all 2048 x n outputs of every matrix (29.4 M per matrix) against fp64
+    for tid, lay, pk, s, z in llama_ffn:
         x = synth.activations(synth.rng_for(4, r), 2048, lay.k, "bf16")
         y = mq.linear(x.to(DEV), pk, r, O.PREFIX, 128, s, z)
-        check_y(y, lay, x, r, O.PREFIX, rows=sample_rows(lay.n, 16))
+        check_y(y, lay, x, r, O.PREFIX, w64=w64_of(tid, lay, r, O.PREFIX))
 
 
 @pytest.mark.parametrize("m,dt", [(1, "f16"), (256, "bf16")])
@@ -322,12 +394,12 @@ def test_gemma_mixnmatch_blocks(mq, m, dt):
             lay = synth.make_layer(cfg_id=5, tensor_id=tid, n=n, k=k, m=0, group=128, extra=(blk,))
             q, s, z = to_dev(lay)
             x = synth.activations(synth.rng_for(5, 50 + tid, blk, m), m, k, dt)
-            calls.append(mq.Call(x=x.to(DEV), packed=mq.pack_parent(q), r=r, rule=O.PREFIX, group=128,
-                                 scales=s, zeros=z))
+            calls.append(mq.Call(x=x.to(DEV), packed=mq.pack_parent(q).truncated(r), r=r, rule=O.PREFIX,
+                                 group=128, scales=s, zeros=z))
             meta.append((lay, x, r))
     outs = mq.linear_mixed(calls)
     for (lay, x, r), y in zip(meta, outs):
-        check_y(y, lay, x, r, O.PREFIX, rows=sample_rows(lay.n, 16))
+        check_y(y, lay, x, r, O.PREFIX)
 
 
 def test_graph_replay_matches_eager(mq):
@@ -356,3 +428,35 @@ def test_graph_replay_matches_eager(mq):
             assert torch.equal(c.out, y0), f"replay {rep} differs"
         mq.linear_mixed(calls[:1])  # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_graph_replay_survives_workspace_growth(mq):
+    # a graph captured with a split-k call keeps the workspace address it was
+    # captured with; a later eager call that needs more workspace must not
+    # free that memory under the graph
+    ws = mq.Workspace()
+    lay = synth.make_layer(cfg_id=7, tensor_id=20, n=512, k=4096, m=24, group=128, x_dtype="f16")
+    q, s, z = to_dev(lay)
+    pk = mq.pack_parent(q)
+    x = lay.x.to(DEV)
+    assert 0 < mq.workspace_bytes(24, 512, 4096) < mq.workspace_bytes(64, 384, 14336)
+    y = torch.empty((24, 512), dtype=torch.float16, device=DEV)
+    mq.linear(x, pk, 3, O.PREFIX, 128, s, z, out=y, workspace=ws)
+    ref = y.clone()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mq.linear(x, pk, 3, O.PREFIX, 128, s, z, out=y, workspace=ws)
+    big = synth.make_layer(cfg_id=7, tensor_id=21, n=384, k=14336, m=64, group=128, x_dtype="f16")
+    qb, sb, zb = to_dev(big)
+    pkb = mq.pack_parent(qb)
+    for rep in range(3):
+        yb = mq.linear(big.x.to(DEV), pkb, 4, O.PREFIX, 128, sb, zb, workspace=ws)  # grows the workspace
+        filler = torch.full((1 << 22,), 7.0, device=DEV)  # reuses freed memory, if any was freed
+        y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref), f"replay {rep} differs"
+        del filler
+    check_y(yb, big, big.x, 4, O.PREFIX)
+    check_y(y, lay, lay.x, 3, O.PREFIX)

@@ -251,9 +251,46 @@ def test_mixnmatch_recipe_and_mixed_definition():
         calls.append(dict(x=lay.x.double().numpy(), q=lay.q, scales=lay.scales, zeros=lay.zeros,
                           r=r, rule=O.PREFIX, group=128))
     outs = O.linear_mixed(calls)
+    assert [y.shape for y in outs] == [(1, 32)] * 3
+
+
+def _exact_value(q, r, rule):
+    """Reconstructed code-space value read off the binary digits of q, as a
+    Fraction: the top r digits, then (rounded slice) plus the (r+1)-th digit
+    with a clamp at the largest r-bit code, or (true prefix) plus the centre
+    of the 2^(8-r) codes that share the prefix."""
+    b = format(int(q), "08b")
+    top = int(b[:r], 2)
+    if r == 8:
+        return Fraction(top)
+    if rule == O.ROUND:
+        return Fraction(min(top + int(b[r]), 2 ** r - 1) * 2 ** (8 - r))
+    return Fraction(top * 2 ** (8 - r)) + Fraction(2 ** (8 - r) - 1, 2)
+
+
+def test_linear_mixed_brute_force_exact_rationals():
+    # Mix'n'Match (MatQuant summary section 4.3): each layer matrix at its own
+    # width and rule.  Every output is recomputed as an exact rational from the
+    # bit-level definitions, independently of the oracle's arithmetic.
+    specs = [(2, O.ROUND, 64), (6, O.PREFIX, 128), (8, O.ROUND, 64), (3, O.PREFIX, 64), (4, O.ROUND, 128)]
+    calls = []
+    for i, (r, rule, g) in enumerate(specs):
+        lay = synth.make_layer(cfg_id=1, tensor_id=20 + i, n=3, k=128, m=2, group=g, outlier_frac=0.02)
+        calls.append(dict(x=lay.x.double().numpy(), q=lay.q, scales=lay.scales, zeros=lay.zeros,
+                          r=r, rule=rule, group=g))
+    outs = O.linear_mixed(calls)
+    assert len(outs) == len(calls)
     for c, y in zip(calls, outs):
-        np.testing.assert_array_equal(y, O.linear(c["x"], c["q"], c["scales"], c["zeros"], c["r"],
-                                                  c["rule"], c["group"]))
+        assert y.shape == (2, 3)
+        for mi in range(2):
+            for ni in range(3):
+                acc = Fraction(0)
+                for ki in range(128):
+                    gi = ki // c["group"]
+                    v = _exact_value(c["q"][ni, ki], c["r"], c["rule"])
+                    acc += (Fraction(float(c["x"][mi, ki])) * Fraction(float(c["scales"][ni, gi]))
+                            * (v - Fraction(float(c["zeros"][ni, gi]))))
+                assert abs(float(acc) - y[mi, ni]) <= 1e-12 * max(1.0, abs(float(acc)))
 
 
 def test_synth_is_deterministic_and_minmax_in_range():
