@@ -5,42 +5,40 @@ Workload (one step): the Llama-3.1-8B FFN projections (gate and up 4096->14336,
 down 14336->4096) at decode batch M = 1, fp16 activations, one int8 parent
 per matrix (g = 128, fp16 scale/zero, W ~ N(0, 0.02^2) with 0.1% outliers x10),
 sliced with the true-prefix rule at every width r in {2, 3, 4, 6, 8}: 15 layer
-calls, issued as one mixed-width call per width.  Within such a call the
-library runs the independent gate and up calls (one shape class) as one GEMV
-launch and down as a second one.
+calls, issued as one mixed-width call list per width.  Each projection reads a
+fixed seeded input and writes its own output, so the three calls of a width
+are independent and the library runs them as one GEMV launch.
 
 Inputs are resident in HBM before timing.  Each step reads a different copy of
-the parents from a ring whose bytes read per pass exceed the 256 MB MALL, so
-weight reads come from HBM, not the last-level cache.
+the parents from a ring sized so that every timed piece reads more than 1 GiB
+per pass through it (four times the 256 MB MALL): weight reads come from HBM,
+not the last-level cache.
 
-Printed JSON (one line): value = algorithmic bytes of all calls / wall time of
-the timed steps (GB/s).  Algorithmic bytes per call = bit planes the width
-reads + 4 B (fp16 scale + zero) per group + X (2*M*K) + Y (2*M*N).  The timed
-steps are timed twice: replayed from HIP graphs that each hold `ring`
-consecutive steps in the eager order (checked bit for bit against the eager
-calls before timing), and issued as one C-ABI call per width (`eager`, host
-launch gaps included); `graph` and `eager` are both reported and `value` is the
-faster of the two (`timing` names it).  `roofline` is for the
-kernel launch that takes the most time per step (the r = 8 GEMV launch that
-serves gate and up together): its bytes per launch over its average launch
-duration, from HIP events on the launch stream around replays of a graph of
-those launches only.  `per_r` gives the same figures for every width and both
-launches of the step, plus the gate call launched alone for comparison.
-`prefill` times the M = 2048 bf16 prefill
-GEMM (same shapes, r in {2, 4, 8}) against the dense bf16 MFMA peak.
-`skinny` times decode batches M in {8, 16, 32, 64} at r in {2, 3, 4, 8} on the
-same shapes against max(HBM time, MFMA time).  `mixnmatch` times one pass over
-42 Gemma-2-9B FFN blocks (gate/up 3584->14336, down 14336->3584, g = 128) with
-the seeded per-block widths (14 each of 2, 3 and 4 bits) at M = 1 (fp16) and
-M = 256 (bf16), replayed from one HIP graph per pass (eager figure kept); those
-parents are drawn on the device (same recipe).
-`cpu_baseline` times the CPU oracle on all three matrices at every width.
+Timing (one declared mode): the calls are captured in HIP graphs (checked bit
+for bit against eager calls first) and replayed; HIP events on the launch
+stream bracket the replays.
+  value        algorithmic bytes of all calls of the timed steps / their time
+               (GB/s).  Algorithmic bytes per call = bit planes the width reads
+               + 4 B (fp16 scale + zero) per group + X (2*M*K) + Y (2*M*N).
+  per_r        per width: the one launch of the step (gate, up and down), and
+               the two launches a dependent FFN block needs (gate+up, then
+               down reading their product), each averaged over >= 200 launches.
+  roofline     the launch with the most time per step (r = 8).
+  prefill      the M = 2048 bf16 GEMM (same shapes, r in {2, 4, 8}).
+  skinny       decode batches M in {8, 16, 32, 64} at r in {2, 3, 4, 8}
+               against max(HBM time, MFMA time).
+  mixnmatch    one pass over 42 Gemma-2-9B FFN blocks (gate/up 3584->14336,
+               down 14336->3584, g = 128) at the seeded per-block widths (14
+               each of 2, 3 and 4 bits), M = 1 (fp16) and M = 256 (bf16); each
+               call reads a fixed input and writes its own output.
+  cpu_baseline the CPU oracle on all three matrices at every width.
 """
 from __future__ import annotations
 
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -55,11 +53,13 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 WIDTHS = (2, 3, 4, 6, 8)
 PREFILL_WIDTHS = (2, 4, 8)
 GROUP = 128
+RING_BYTES = 1 << 30           # bytes each timed piece reads per pass through the ring
+MIN_LAUNCHES = 200             # launches averaged per per-launch figure
 METRIC = "sliced W·X: decode GB/s (packed bytes, %HBM peak) + prefill TFLOP/s (%MFMA) per r"
 PLANE_BITS = (2, 1, 1, 2, 2)
 PLANES_FOR_R = {2: 1, 3: 2, 4: 3, 6: 4, 8: 5}
 DECODE_KERNEL_SRC = os.path.join(ROOT, "nested_integer_weight_amd", "csrc", "mq_gemv.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_batch_r8_llama8b_gate_up_m1.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_r8_llama8b_ffn_m1.json")
 
 
 def log(msg):
@@ -76,19 +76,28 @@ def src_hash(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--ring", type=int, default=8, help="distinct parent copies cycled through")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--eager", action="store_true", help="time eager calls only (no HIP graph replay)")
     ap.add_argument("--cpu-steps", type=int, default=3, help="workload steps the CPU oracle baseline times")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill GEMM lines")
     ap.add_argument("--prefill-iters", type=int, default=10)
     ap.add_argument("--no-skinny", action="store_true", help="skip the M in {8,16,32,64} lines")
     ap.add_argument("--no-mix", action="store_true", help="skip the 42-block Mix'n'Match stack lines")
+    ap.add_argument("--no-pieces", action="store_true", help="skip the per-launch figures")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -105,7 +114,16 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
 
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
     # ---------------- inputs (resident before timing) ----------------
+    # ring: distinct parent copies, enough that the smallest timed piece (the
+    # r = 2 down projection, 16.5 MB) reads > RING_BYTES per pass
+    min_piece = min(alg_bytes(1, n, k, 2) for _, n, k in synth.LLAMA8B_FFN)
+    ring = max(8, math.ceil(RING_BYTES / min_piece))
+    if ring % len(WIDTHS) == 0:
+        ring += 1  # steps walk the ring in strides of len(WIDTHS): keep them coprime
     mats = []
     for tid, (name, n, k) in enumerate(synth.LLAMA8B_FFN):
         t0 = time.time()
@@ -116,165 +134,139 @@ def main():
         z = torch.from_numpy(lay.zeros).to(dev)
         base = mq.pack_parent(q)
         copies = []
-        for c in range(args.ring):
+        for c in range(ring):
             planes = [p.clone() for p in base.planes]
             copies.append((mq.Packed(n, k, planes), s.clone(), z.clone()))
         del q
         mats.append(dict(name=name, n=n, k=k, lay=lay, x=x, xd=x.to(dev), copies=copies,
-                         y=torch.empty((1, n), dtype=torch.float16, device=dev)))
-        log(f"[bench] {name} {n}x{k}: parent packed, {args.ring} copies ({time.time() - t0:.1f}s)")
+                         y={r: torch.empty((1, n), dtype=torch.float16, device=dev) for r in WIDTHS}))
+        log(f"[bench] {name} {n}x{k}: parent packed, {ring} copies ({time.time() - t0:.1f}s)")
     torch.cuda.synchronize()
 
-    def calls_for(step, r):
+    def calls_for(step, r, idx=(0, 1, 2)):
         ri = WIDTHS.index(r)
-        c = (step * len(WIDTHS) + ri) % args.ring
+        c = (step * len(WIDTHS) + ri) % ring
         out = []
-        for mt in mats:
+        for i in idx:
+            mt = mats[i]
             pk, s, z = mt["copies"][c]
             out.append(mq.Call(x=mt["xd"], packed=pk.truncated(r), r=r, rule="prefix", group=GROUP,
-                               scales=s, zeros=z, out=mt["y"]))
+                               scales=s, zeros=z, out=mt["y"][r]))
         return out
 
     bytes_r = {r: sum(alg_bytes(1, mt["n"], mt["k"], r) for mt in mats) for r in WIDTHS}
     bytes_step = sum(bytes_r.values())
-    ring_bytes = sum(bytes_r.values()) * args.ring / len(WIDTHS) * len(WIDTHS)
-    log(f"[bench] bytes/step {bytes_step / 1e6:.1f} MB, ring pass {ring_bytes / 1e9:.2f} GB")
+    log(f"[bench] bytes/step {bytes_step / 1e6:.1f} MB; ring of {ring} copies: "
+        f"{ring * bytes_r[2] / 1e9:.2f} GB per pass at r=2, {ring * bytes_r[8] / 1e9:.2f} GB at r=8")
+
+    def step_calls(step):
+        for r in WIDTHS:
+            mq.linear_mixed(calls_for(step, r))
 
     # ---------------- warmup ----------------
     for i in range(args.warmup):
-        for r in WIDTHS:
-            mq.linear_mixed(calls_for(i, r))
+        step_calls(i)
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} steps done")
 
-    # ---------------- eager timed steps (one C-ABI call per width and step) ----------------
-    def eager_run(n_steps, first):
-        t0_, t1_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        return g
+
+    def outputs():
+        return [mt["y"][r].clone() for mt in mats for r in WIDTHS]
+
+    def check_replay(g, eager_fn):
+        """The graph must reproduce the eager calls bit for bit, replay after
+        replay, with eager work and synchronisation in between."""
+        eager_fn()
         torch.cuda.synchronize()
-        t0_.record(stream)
-        for i in range(n_steps):
-            for r in WIDTHS:
-                mq.linear_mixed(calls_for(first + i, r))
-        t1_.record(stream)
-        torch.cuda.synchronize()
-        return t0_.elapsed_time(t1_)
-
-    eager_ms = eager_run(args.steps, args.warmup)
-    eager = {"value": round(bytes_step * args.steps / (eager_ms * 1e-3) / 1e9, 1),
-             "ms_per_step": round(eager_ms / args.steps, 5)}
-    log(f"[bench] eager {args.steps} steps: {eager['ms_per_step'] * 1e3:.1f} us/step, {eager['value']} GB/s")
-
-    # The step issues two kernel launches per width: mq_linear_mixed runs the
-    # independent gate and up calls (same shape class) as one GEMV launch, and
-    # down as a second one.  Per-launch figures come from graphs (or eager
-    # loops) of one piece at a time, `ring` copies deep.
-    # `gate_alone` (the gate call by itself, one launch) is context: the same
-    # bytes per call without the shared launch.
-    pieces = {"gate_up": [0, 1], "down": [2], "gate_alone": [0]}
-
-    def piece_calls(step, r, idx):
-        allc = calls_for(step, r)
-        return [allc[i] for i in idx]
-
-    def piece_bytes(r, idx):
-        return sum(alg_bytes(1, mats[i]["n"], mats[i]["k"], r) for i in idx)
-
-    def launch_figures(use_graph):
-        out = {}
-        for r in WIDTHS:
-            out[str(r)] = {}
-            for name, idx in pieces.items():
-                reps = max(1, args.steps // args.ring)
-                if use_graph:
-                    g = torch.cuda.CUDAGraph()
-                    with torch.cuda.graph(g):
-                        for i in range(args.ring):
-                            mq.linear_mixed(piece_calls(i, r, idx))
-                    g.replay()
-                    torch.cuda.synchronize()
-                a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a_.record(stream)
-                for _ in range(reps):
-                    if use_graph:
-                        g.replay()
-                    else:
-                        for i in range(args.ring):
-                            mq.linear_mixed(piece_calls(i, r, idx))
-                b_.record(stream)
-                torch.cuda.synchronize()
-                us = a_.elapsed_time(b_) * 1e3 / (reps * args.ring)
-                byt = piece_bytes(r, idx)
-                gbs = byt / (us * 1e-6) / 1e9
-                out[str(r)][name] = {"us_per_launch": round(us, 3), "bytes_per_launch": int(byt),
-                                     "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
-                if use_graph:
-                    del g
-        return out
-
-    # ---------------- HIP graph replay (the serving form of the step) ----------------
-    # One graph holds `ring` consecutive steps in the eager order of widths and
-    # parent copies, so each replay still reads every weight byte from HBM; the
-    # host issues one launch per `ring` steps instead of one call per width.
-    graph, graph_ok = None, False
-    timed_steps = args.steps
-    if not args.eager:
-        ring = args.ring
-        # eager reference of the last step of the ring, then the graph's last step must match it
-        for r in WIDTHS:
-            mq.linear_mixed(calls_for(ring - 1, r))
-        torch.cuda.synchronize()
-        ref = [mt["y"].clone() for mt in mats]
-        g_step = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g_step):
-            for i in range(ring):
-                for r in WIDTHS:
-                    mq.linear_mixed(calls_for(i, r))
-        rem = args.steps % ring  # leftover steps, so that exactly --steps steps are timed
-        g_rem = None
-        if rem:
-            g_rem = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g_rem):
-                for i in range(rem):
-                    for r in WIDTHS:
-                        mq.linear_mixed(calls_for(i, r))
-        ok = True
-        for rep in range(2):  # replays interleaved with eager work and synchronisation
+        ref = outputs()
+        for _ in range(2):
             for mt in mats:
-                mt["y"].zero_()
-            g_step.replay()
+                for r in WIDTHS:
+                    mt["y"][r].zero_()
+            g.replay()
             torch.cuda.synchronize()
-            ok = ok and all(torch.equal(mt["y"], y0) for mt, y0 in zip(mats, ref))
-            mq.linear_mixed(calls_for(0, 2))
+            if not all(torch.equal(a, b) for a, b in zip(outputs(), ref)):
+                return False
+            eager_fn()
             torch.cuda.synchronize()
-        if not ok:
-            log("[bench] graph replay differs from the eager step: reporting eager timing")
-        else:
-            reps = args.steps // ring
-            timed_steps = args.steps
-            t0_, t1_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            t0_.record(stream)
-            for _ in range(reps):
-                g_step.replay()
-            if g_rem is not None:
-                g_rem.replay()
-            t1_.record(stream)
-            torch.cuda.synchronize()
-            g_ms = t0_.elapsed_time(t1_)
-            graph = {"value": round(bytes_step * timed_steps / (g_ms * 1e-3) / 1e9, 1),
-                     "ms_per_step": round(g_ms / timed_steps, 5)}
-            graph_ok = True
-            log(f"[bench] graph {timed_steps} steps: {graph['ms_per_step'] * 1e3:.1f} us/step, {graph['value']} GB/s")
-        del g_step, g_rem
-    # `value`: the faster of the two issue forms of the same timed steps (both
-    # reported); with two launches per width the host keeps ahead of the GPU,
-    # so eager calls and graph replay take about the same time
-    if graph is not None and graph["value"] >= eager["value"]:
-        mode, value, ms_per_step = "hip_graph", graph["value"], graph["ms_per_step"]
-    else:
-        mode, value, ms_per_step = "eager", eager["value"], eager["ms_per_step"]
-    per_r = launch_figures(graph_ok)
-    dom = per_r["8"]["gate_up"]
+        return True
+
+    # ---------------- timed steps: HIP graph replay ----------------
+    # One graph holds `gsteps` consecutive steps of the ring; the timed region
+    # replays it, plus one graph of the leftover steps, so exactly --steps
+    # steps are timed and consecutive steps read different parent copies.
+    gsteps = min(args.steps, ring)
+    g_step = capture(lambda: [step_calls(i) for i in range(gsteps)])
+    if not check_replay(g_step, lambda: [step_calls(i) for i in range(gsteps)]):
+        raise RuntimeError("graph replay of the decode step differs from the eager calls")
+    rem = args.steps % gsteps
+    g_rem = capture(lambda: [step_calls(i) for i in range(rem)]) if rem else None
+    torch.cuda.synchronize()
+    t0_, t1_ = ev(), ev()
+    t0_.record(stream)
+    for _ in range(args.steps // gsteps):
+        g_step.replay()
+    if g_rem is not None:
+        g_rem.replay()
+    t1_.record(stream)
+    torch.cuda.synchronize()
+    step_ms = t0_.elapsed_time(t1_) / args.steps
+    value = bytes_step / (step_ms * 1e-3) / 1e9
+    log(f"[bench] {args.steps} steps (graph replay): {step_ms * 1e3:.1f} us/step, {value:.1f} GB/s")
+    del g_step, g_rem
+
+    # secondary: the same steps issued as eager C-ABI calls (host gaps included)
+    torch.cuda.synchronize()
+    t0_.record(stream)
+    for i in range(args.steps):
+        step_calls(args.warmup + i)
+    t1_.record(stream)
+    torch.cuda.synchronize()
+    eager_ms = t0_.elapsed_time(t1_) / args.steps
+    eager = {"value": round(bytes_step / (eager_ms * 1e-3) / 1e9, 1), "ms_per_step": round(eager_ms, 5)}
+    log(f"[bench] eager: {eager_ms * 1e3:.1f} us/step")
+
+    # ---------------- per-launch figures ----------------
+    # The fused launch of each width (gate, up and down), and for comparison the
+    # two launches of a dependent FFN block, where down reads what gate and up
+    # produced and so cannot share their launch: gate and up, then down alone.
+    # Graphs of `ring` launches over the whole ring, replayed until >= 200.
+    def piece(fn_for_step, nbytes):
+        g = capture(lambda: [fn_for_step(i) for i in range(ring)])
+        g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, math.ceil(MIN_LAUNCHES / ring))
+        a_, b_ = ev(), ev()
+        a_.record(stream)
+        for _ in range(reps):
+            g.replay()
+        b_.record(stream)
+        torch.cuda.synchronize()
+        us = a_.elapsed_time(b_) * 1e3 / (reps * ring)
+        del g
+        gbs = nbytes / (us * 1e-6) / 1e9
+        return {"us_per_launch": round(us, 3), "bytes_per_launch": int(nbytes), "GB/s": round(gbs, 1),
+                "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "launches_timed": reps * ring}
+
+    per_r = {}
+    if not args.no_pieces:
+        for r in WIDTHS:
+            d = {}
+            d["gate_up_down"] = piece(lambda i: mq.linear_mixed(calls_for(i, r)), bytes_r[r])
+            gu = sum(alg_bytes(1, mats[i]["n"], mats[i]["k"], r) for i in (0, 1))
+            d["gate_up"] = piece(lambda i: mq.linear_mixed(calls_for(i, r, (0, 1))), gu)
+            d["down"] = piece(lambda i: mq.linear_mixed(calls_for(i, r, (2,))), bytes_r[r] - gu)
+            dep_us = d["gate_up"]["us_per_launch"] + d["down"]["us_per_launch"]
+            d["dependent_ffn_block"] = {"us": round(dep_us, 3),
+                                        "frac_hbm": round(bytes_r[r] / (dep_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+            per_r[str(r)] = d
+            log(f"[bench] r={r}: one launch {d['gate_up_down']['us_per_launch']} us "
+                f"({d['gate_up_down']['frac_hbm'] * 100:.1f}% HBM); dependent block {dep_us:.2f} us")
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -284,12 +276,14 @@ def main():
                 traffic = t.get("hbm_bytes_per_launch")
         except Exception:
             traffic = None
-
-    roofline = {"bound": "hbm", "achieved": dom["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(dom["GB/s"] / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "mq::gemv_batch_kernel<r=8, prefix, m=1, fp16>: gate and up (2 x 14336x4096) in one "
-                          "launch (mq_linear_mixed decode path)",
-                "bytes_per_launch": dom["bytes_per_launch"], "us_per_launch": dom["us_per_launch"]}
+    roofline = None
+    if per_r:
+        dom = per_r["8"]["gate_up_down"]
+        roofline = {"bound": "hbm", "achieved": dom["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(dom["GB/s"] / HBM_PEAK_GBS, 4), "traffic": traffic,
+                    "kernel": "mq::gemv_multi_kernel<r=8, prefix, m=1, fp16>: gate, up (14336x4096) and down "
+                              "(4096x14336) in one launch (mq_linear_mixed decode path)",
+                    "bytes_per_launch": dom["bytes_per_launch"], "us_per_launch": dom["us_per_launch"]}
 
     # ---------------- prefill (M = 2048, bf16) ----------------
     prefill = None
@@ -299,16 +293,16 @@ def main():
         for r in PREFILL_WIDTHS:
             rows = []
             for mt in mats:
-                pk, s, z = mt["copies"][0]
                 x = xs[mt["k"]]
                 y = torch.empty((2048, mt["n"]), dtype=torch.bfloat16, device=dev)
-                for _ in range(2):
+                for c in range(2):
+                    pk, s, z = mt["copies"][c]
                     mq.linear(x, pk, r, "prefix", GROUP, s, z, out=y)
                 torch.cuda.synchronize()
-                a = torch.cuda.Event(enable_timing=True)
-                b = torch.cuda.Event(enable_timing=True)
+                a, b = ev(), ev()
                 a.record(stream)
-                for _ in range(args.prefill_iters):
+                for it in range(args.prefill_iters):
+                    pk, s, z = mt["copies"][it % ring]
                     mq.linear(x, pk, r, "prefix", GROUP, s, z, out=y)
                 b.record(stream)
                 torch.cuda.synchronize()
@@ -331,16 +325,15 @@ def main():
             ys_m = {n: torch.empty((m, n), dtype=torch.float16, device=dev) for n in (4096, 14336)}
             for r in (2, 3, 4, 8):
                 def sk_calls(it):
-                    c = it % args.ring
+                    c = it % ring
                     return [mq.Call(x=xs_m[mt["k"]], packed=mt["copies"][c][0].truncated(r), r=r, rule="prefix",
                                     group=GROUP, scales=mt["copies"][c][1], zeros=mt["copies"][c][2],
                                     out=ys_m[mt["n"]]) for mt in mats]
                 for i in range(3):
                     mq.linear_mixed(sk_calls(i))
                 torch.cuda.synchronize()
-                iters = 2 * args.ring
-                a_ = torch.cuda.Event(enable_timing=True)
-                b_ = torch.cuda.Event(enable_timing=True)
+                iters = max(ring, math.ceil(MIN_LAUNCHES / len(mats)))
+                a_, b_ = ev(), ev()
                 a_.record(stream)
                 for i in range(iters):
                     mq.linear_mixed(sk_calls(3 + i))
@@ -374,58 +367,40 @@ def main():
         mix = {"widths": widths, "mean_bits": sum(widths) / len(widths)}
         for m, dt, tdt in ((1, "f16", torch.float16), (256, "bf16", torch.bfloat16)):
             xk = {k: synth.activations(synth.rng_for(5, 77, k, m), m, k, dt).to(dev) for k in (3584, 14336)}
-            # each projection writes its own output, as in an FFN block (gate and
-            # up then form the input of down); the buffers are reused across blocks
-            yn = {(name, n): torch.empty((m, n), dtype=tdt, device=dev) for name, n, _ in synth.GEMMA9B_FFN}
-            calls = [mq.Call(x=xk[k], packed=pk, r=r, rule="prefix", group=GROUP, scales=s_, zeros=z_,
-                             out=yn[(name, n)])
-                     for (blk, name, n, k, r, pk, s_, z_) in blocks]
+            ys = [torch.empty((m, n), dtype=tdt, device=dev) for (_, _, n, _, _, _, _, _) in blocks]
+            calls = [mq.Call(x=xk[k], packed=pk, r=r, rule="prefix", group=GROUP, scales=s_, zeros=z_, out=y)
+                     for (blk, name, n, k, r, pk, s_, z_), y in zip(blocks, ys)]
             mq.linear_mixed(calls)
             torch.cuda.synchronize()
+            ref = [y.clone() for y in ys]
+            g = capture(lambda: mq.linear_mixed(calls))
+            for y in ys:
+                y.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            if not all(torch.equal(a, b) for a, b in zip(ys, ref)):
+                raise RuntimeError("graph replay of the Mix'n'Match pass differs from the eager calls")
             passes = 5 if m == 1 else 3
-            a_ = torch.cuda.Event(enable_timing=True)
-            b_ = torch.cuda.Event(enable_timing=True)
+            a_, b_ = ev(), ev()
             a_.record(stream)
             for _ in range(passes):
-                mq.linear_mixed(calls)
+                g.replay()
             b_.record(stream)
             torch.cuda.synchronize()
             us = a_.elapsed_time(b_) * 1e3 / passes
-            eager_us = us
-            mode_mix = "eager"
-            if not args.eager:
-                # the same pass replayed from one HIP graph (checked bit for bit first)
-                ref = {nn: yy.clone() for nn, yy in yn.items()}
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g):
-                    mq.linear_mixed(calls)
-                for yy in yn.values():
-                    yy.zero_()
-                g.replay()
-                torch.cuda.synchronize()
-                if all(torch.equal(yn[nn], ref[nn]) for nn in yn):
-                    a_.record(stream)
-                    for _ in range(passes):
-                        g.replay()
-                    b_.record(stream)
-                    torch.cuda.synchronize()
-                    us = a_.elapsed_time(b_) * 1e3 / passes
-                    mode_mix = "hip_graph"
-                else:
-                    log("[bench] mixnmatch graph replay differs from the eager pass: reporting eager timing")
-                del g
+            del g
             byt = sum(alg_bytes(m, n, k, r) for (blk, name, n, k, r, pk, s_, z_) in blocks)
             fl = 2.0 * m * sum(n * k for (blk, name, n, k, r, pk, s_, z_) in blocks)
             if m == 1:
                 mix["m1"] = {"us_per_pass": round(us, 1), "GB/s": round(byt / (us * 1e-6) / 1e9, 1),
-                             "frac_hbm": round(byt / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "bytes": int(byt),
-                             "timing": mode_mix, "eager_us_per_pass": round(eager_us, 1)}
+                             "frac_hbm": round(byt / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "bytes": int(byt)}
             else:
                 mix["m256"] = {"us_per_pass": round(us, 1), "TFLOP/s": round(fl / (us * 1e-6) / 1e12, 1),
                                "frac_mfma_bf16": round(fl / (us * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
-                               "flop": fl, "timing": mode_mix, "eager_us_per_pass": round(eager_us, 1)}
-            log(f"[bench] mixnmatch m={m}: {us:.1f} us per pass of {len(blocks)} calls ({mode_mix}; eager {eager_us:.1f})")
-        del blocks, calls
+                               "flop": fl}
+            log(f"[bench] mixnmatch m={m}: {us:.1f} us per pass of {len(blocks)} calls (graph replay)")
+            del ys, calls, ref
+        del blocks
 
     if args.copy_calib_mib > 0:
         nb = args.copy_calib_mib << 20
@@ -438,41 +413,61 @@ def main():
     # ---------------- CPU oracle baseline ----------------
     cpu = None
     if not args.no_cpu:
+        from threadpoolctl import threadpool_info, threadpool_limits
+
         from oracle import mq_oracle as O
-        try:
-            from threadpoolctl import threadpool_info
-            blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-        except Exception:
-            blas_threads = 1
+
+        def oracle_calls(n_steps):
+            done = 0
+            for _ in range(n_steps):
+                for mt in mats:
+                    lay = mt["lay"]
+                    x64 = mt["x"].double().numpy()
+                    for r in WIDTHS:
+                        O.linear(x64, lay.q, lay.scales, lay.zeros, r, O.PREFIX, GROUP)
+                        done += alg_bytes(1, mt["n"], mt["k"], r)
+            return done
+
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
         t0 = time.perf_counter()
-        done = 0
-        for _ in range(args.cpu_steps):
-            for mt in mats:
-                lay = mt["lay"]
-                x64 = mt["x"].double().numpy()
-                for r in WIDTHS:
-                    O.linear(x64, lay.q, lay.scales, lay.zeros, r, O.PREFIX, GROUP)
-                    done += alg_bytes(1, mt["n"], mt["k"], r)
+        done = oracle_calls(args.cpu_steps)
         dt = time.perf_counter() - t0
+        # single thread: config 1 (512 x 512, g = 64, both rules at r in {8, 4, 2}) and one step of config 2
+        with threadpool_limits(limits=1):
+            c1 = synth.make_layer(cfg_id=1, tensor_id=0, n=512, k=512, m=1, group=64, x_dtype="f16")
+            x1 = c1.x.double().numpy()
+            t1 = time.perf_counter()
+            for r in (8, 4, 2):
+                for rule in (O.PREFIX, O.ROUND):
+                    O.linear(x1, c1.q, c1.scales, c1.zeros, r, rule, 64)
+            c1_s = time.perf_counter() - t1
+            t2 = time.perf_counter()
+            done1 = oracle_calls(1)
+            st_dt = time.perf_counter() - t2
         cpu = {"value": round(done / dt / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
                "sample": f"oracle (numpy fp64 slice + dequant + matmul) on {args.cpu_steps} steps of the "
                          f"workload: gate, up and down at M=1 for r in {list(WIDTHS)} "
-                         f"({15 * args.cpu_steps} calls), {dt:.1f} s"}
-        log(f"[bench] cpu oracle: {cpu['value']} GB/s in {dt:.1f}s")
+                         f"({15 * args.cpu_steps} calls), {dt:.1f} s; elementwise numpy on one thread, "
+                         f"BLAS on {blas_threads}",
+               "host_cores": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
+               "single_thread": {"config1_s_for_6_calls": round(c1_s, 4),
+                                 "config2_GB/s": round(done1 / st_dt / 1e9, 4)}}
+        log(f"[bench] cpu oracle: {cpu['value']} GB/s in {dt:.1f}s ({blas_threads} BLAS threads)")
 
     out = {
-        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": timed_steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(step_ms, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
-        "config": {"workload": "llama3.1-8b-ffn decode: gate/up 4096->14336 (one launch) + down 14336->4096, M=1, "
-                               "g=128, true-prefix, r in {2,3,4,6,8}",
-                   "global_batch": 1, "widths": list(WIDTHS), "ring_copies": args.ring},
+        "config": {"workload": "llama3.1-8b-ffn decode: gate/up 4096->14336 + down 14336->4096, M=1, g=128, "
+                               "true-prefix, r in {2,3,4,6,8}, one launch per width",
+                   "global_batch": 1, "widths": list(WIDTHS), "ring_copies": ring},
+        "timing": "hip_graph_replay",
         "roofline": roofline,
-        "timing": mode,
-        "eager": eager,
-        "graph": graph,
-        "per_r": per_r,
+        "frac_hbm_per_r": {r: v["gate_up_down"]["frac_hbm"] for r, v in per_r.items()},
+        "frac_hbm_step": round(value / HBM_PEAK_GBS, 4),
         "prefill": prefill,
+        "per_r": per_r,
+        "eager": eager,
         "skinny": skinny,
         "mixnmatch": mix,
         "cpu_baseline": cpu,

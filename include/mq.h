@@ -156,15 +156,20 @@ mq_status mq_linear(const void* x, int32_t x_dtype, int32_t m, const mq_packed* 
                     void* y, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Mix'n'Match ("Matryoshka Quantization | Summary", section 4.3): n_calls
- * layer matrices, each at its own width, issued in order on one stream and
- * sharing one workspace.  All calls are validated before the first launch; an
- * invalid call returns its status and nothing is launched.  *failed_call (if
- * not NULL) receives the index of the first invalid call, else -1.
- * Consecutive calls that take the register GEMV with the same m, k, width,
- * rule, group and dtype, and whose outputs overlap neither each other nor the
- * others' inputs, run in one launch (up to 4 calls; e.g. the gate and up
- * projections of a decode step).  The results are those of issuing the calls
- * in order; a launch error reports the first call of its launch. */
+ * layer matrices, each at its own width, issued on one stream and sharing one
+ * workspace.  All calls are validated before the first launch; an invalid call
+ * returns its status and nothing is launched.  *failed_call (if not NULL)
+ * receives the index of the first invalid call, else -1.
+ * The list is cut into runs of consecutive calls that are pairwise
+ * independent (no call writes memory that another call of the run reads or
+ * writes: x, the planes its width needs, scales, zeros, y).  Runs execute in
+ * order.  Inside a run, every call that takes the register GEMV (fp16 x with
+ * m <= 4, bf16 x with m == 1, k <= 16384) with the same m, width, rule and
+ * dtype joins one launch (up to 32 calls of any shape, e.g. the gate, up and
+ * down projections of a decode step, or the projections of several
+ * Mix'n'Match blocks); the other calls run one by one.  The results are those
+ * of issuing the calls in order, bit for bit.  A launch error reports the
+ * first call of its launch. */
 mq_status mq_linear_mixed(const mq_call* calls, int32_t n_calls, void* workspace,
                           size_t workspace_bytes, int32_t* failed_call, void* stream);
 

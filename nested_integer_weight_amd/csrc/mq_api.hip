@@ -87,7 +87,7 @@ mq_status run_linear(const void* x, int x_dtype, int m, const mq_packed* w, int 
   a.bf16 = x_dtype == MQ_BF16;
   hipError_t e;
   if (gemv_eligible(m, w->k, a.bf16)) {
-    e = launch_gemv(a, s);
+    e = launch_gemv_multi(&a, 1, s);
   } else if (skinny_eligible(m, w->k)) {
     const bool ws_ok = workspace && aligned16(workspace);
     e = launch_skinny(a, ws_ok ? workspace : nullptr, ws_ok ? workspace_bytes : 0, s);
@@ -107,20 +107,31 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 size_t x_bytes(const mq_call& c) { return (size_t)c.m * (size_t)c.w->k * 2; }
 size_t y_bytes(const mq_call& c) { return (size_t)c.m * (size_t)c.w->n * 2; }
 
-// May call d join a single GEMV launch with call c (c issued before d)?  They
-// must share the shape class of the launch (m, k, width, rule, group, dtype)
-// and be independent: neither output may overlap the other call's input or
-// output, so running both at once gives what running them in order gives.
-bool can_batch(const mq_call& c, const mq_call& d) {
-  if (c.m != d.m || c.m == 0 || c.w->k != d.w->k || c.r != d.r || c.rule != d.rule || c.group != d.group ||
-      c.x_dtype != d.x_dtype)
-    return false;
-  if (!gemv_eligible(c.m, c.w->k, c.x_dtype == MQ_BF16)) return false;
-  return !overlaps(c.y, y_bytes(c), d.x, x_bytes(d)) && !overlaps(d.y, y_bytes(d), c.x, x_bytes(c)) &&
-         !overlaps(c.y, y_bytes(c), d.y, y_bytes(d));
+// Does call c write anything that call d reads or writes?  d reads x, the
+// planes its width needs, the scales and the zero points, and writes y.
+bool writes_into(const mq_call& c, const mq_call& d) {
+  const size_t yc = y_bytes(c);
+  if (overlaps(c.y, yc, d.x, x_bytes(d)) || overlaps(c.y, yc, d.y, y_bytes(d))) return true;
+  const size_t sz = (size_t)d.w->n * (size_t)(d.w->k / d.group) * 2;
+  if (overlaps(c.y, yc, d.scales, sz) || overlaps(c.y, yc, d.zeros, sz)) return true;
+  const int np = planes_needed(d.r, d.rule == MQ_ROUND);
+  for (int p = 0; p < np; ++p)
+    if (overlaps(c.y, yc, d.w->plane[p], (size_t)d.w->n * (size_t)d.w->k * kPlaneBits[p] / 8)) return true;
+  return false;
 }
 
-LinearArgs gemv_args(const mq_call& c, const PlanePtrs& pl) {
+// Calls that neither write what the other reads or writes give the same
+// results in any order or at the same time.
+bool independent(const mq_call& c, const mq_call& d) { return !writes_into(c, d) && !writes_into(d, c); }
+
+// The launch class of a GEMV-eligible call: calls of one class can share a
+// GEMV launch.
+bool same_gemv_class(const mq_call& c, const mq_call& d) {
+  return c.m == d.m && c.r == d.r && c.rule == d.rule && c.x_dtype == d.x_dtype;
+}
+bool gemv_call(const mq_call& c) { return c.m > 0 && gemv_eligible(c.m, c.w->k, c.x_dtype == MQ_BF16); }
+
+LinearArgs call_args(const mq_call& c, const PlanePtrs& pl) {
   LinearArgs a;
   a.x = c.x;
   a.y = c.y;
@@ -136,6 +147,15 @@ LinearArgs gemv_args(const mq_call& c, const PlanePtrs& pl) {
   a.bf16 = c.x_dtype == MQ_BF16;
   return a;
 }
+
+PlanePtrs planes_of(const mq_call& c) {
+  PlanePtrs pl;
+  for (int p = 0; p < MQ_NPLANES; ++p) pl.p[p] = static_cast<const uint32_t*>(c.w->plane[p]);
+  return pl;
+}
+
+// calls looked at together when forming launches
+constexpr int kWindow = 256;
 
 }  // namespace
 
@@ -214,35 +234,41 @@ mq_status mq_linear_mixed(const mq_call* calls, int32_t n_calls, void* workspace
       return st;
     }
   }
+  // Runs of consecutive, pairwise independent calls: inside a run the order
+  // does not matter, so every GEMV-eligible call of one class (m, width,
+  // rule, dtype) goes into one launch, whatever its shape, and the other calls
+  // run one by one.  Runs follow each other in stream order.
   for (int32_t i = 0; i < n_calls;) {
-    const mq_call& c = calls[i];
-    PlanePtrs pl;
-    validate_linear(c.x, c.x_dtype, c.m, c.w, c.r, c.rule, c.group, c.scales, c.zeros, c.y, &pl);
-    // consecutive independent GEMV calls of one shape class share a launch
     int32_t j = i + 1;
-    while (j < n_calls && j - i < kGemvMaxBatch) {
+    while (j < n_calls && j - i < kWindow) {
       bool ok = true;
-      for (int32_t t = i; t < j && ok; ++t) ok = can_batch(calls[t], calls[j]);
+      for (int32_t t = i; t < j && ok; ++t) ok = independent(calls[t], calls[j]);
       if (!ok) break;
       ++j;
     }
-    mq_status st;
-    if (j - i > 1) {
-      LinearArgs la[kGemvMaxBatch];
-      for (int32_t t = i; t < j; ++t) {
-        PlanePtrs plt;
-        const mq_call& ct = calls[t];
-        validate_linear(ct.x, ct.x_dtype, ct.m, ct.w, ct.r, ct.rule, ct.group, ct.scales, ct.zeros, ct.y, &plt);
-        la[t - i] = gemv_args(ct, plt);
+    bool done[kWindow] = {};
+    for (int32_t t = i; t < j; ++t) {
+      if (done[t - i]) continue;
+      const mq_call& c = calls[t];
+      mq_status st;
+      if (gemv_call(c)) {
+        LinearArgs la[kGemvMaxCalls];
+        int nl = 0;
+        for (int32_t u = t; u < j && nl < kGemvMaxCalls; ++u) {
+          if (done[u - i] || !gemv_call(calls[u]) || !same_gemv_class(c, calls[u])) continue;
+          la[nl++] = call_args(calls[u], planes_of(calls[u]));
+          done[u - i] = true;
+        }
+        st = launch_gemv_multi(la, nl, static_cast<hipStream_t>(stream)) == hipSuccess ? MQ_OK : MQ_EHIP;
+      } else {
+        done[t - i] = true;
+        st = run_linear(c.x, c.x_dtype, c.m, c.w, c.r, c.rule, c.group, c.scales, c.zeros, c.y, workspace,
+                        workspace_bytes, planes_of(c), static_cast<hipStream_t>(stream));
       }
-      st = launch_gemv_batch(la, j - i, static_cast<hipStream_t>(stream)) == hipSuccess ? MQ_OK : MQ_EHIP;
-    } else {
-      st = run_linear(c.x, c.x_dtype, c.m, c.w, c.r, c.rule, c.group, c.scales, c.zeros, c.y, workspace,
-                      workspace_bytes, pl, static_cast<hipStream_t>(stream));
-    }
-    if (st != MQ_OK) {
-      if (failed_call) *failed_call = i;
-      return st;
+      if (st != MQ_OK) {
+        if (failed_call) *failed_call = t;
+        return st;
+      }
     }
     i = j;
   }

@@ -1,43 +1,82 @@
-// mq_gemv.hip -- decode path (m <= 4): stream the bit planes, rebuild and
-// slice the codes in registers, contract with register-resident activations,
-// reduce across lanes with a transposing butterfly.
+// mq_gemv.hip -- decode path (m <= 4): stream the bit planes of one or more
+// independent layer calls in one launch, rebuild and slice the codes in
+// registers, contract with register-resident activations, reduce across lanes
+// with a transposing butterfly.
 //
-// The pages' small-batch design streams weights straight from memory because
-// decoding at batch <= 4 is memory-bandwidth bound (MatGPTQ "Efficient and
-// Accurate Inference over Nested Quantized Models", section 4, third
-// component).  On gfx950 this becomes:
-//  * every lane owns a fixed 64-code k-slice (two packing units) and walks a
-//    block of output rows, so its slice of X is loaded once into VGPRs and
-//    reused for every row; per row a lane issues one 16-byte load per 2-bit
-//    plane and one 8-byte load per 1-bit plane, and the 64 lanes of a wave
-//    cover consecutive slices, so each load instruction reads contiguous bytes;
-//  * fp16 activations: a code byte v becomes the exact fp16 1024+v with one
-//    v_perm_b32 (the byte under an 0x64 exponent byte) and v_dot2_f32_f16
-//    accumulates X.(1024+v) in fp32; the 1024 and the zero point are removed
-//    per (row, slice) with the slice's sum of X:
+// The pages' small-batch design streams the weights straight from memory,
+// because decoding at batch <= 4 is bound by memory bandwidth (MatGPTQ
+// "Efficient and Accurate Inference over Nested Quantized Models", section
+// 4, third component).  On gfx950:
+//  * Work items.  Every call's output rows are cut into items of 4 / W row
+//    groups x ROWS rows; a row group is W waves (W = 1, 2 or 4 by k), each
+//    lane owning a fixed 64-code k-slice of the group's rows, so its slice of
+//    X sits in VGPRs for every row it walks.  One 256-thread workgroup per
+//    item; a launch covers the items of up to kGemvMaxCalls calls of one
+//    width, rule, m and dtype (any n, k and group), found by a scalar search
+//    of the kernel arguments.  Independent calls (gate, up and down of an FFN
+//    at one width, or a whole Mix'n'Match pass) then share one launch ramp
+//    and drain.
+//  * Loads.  Buffer loads: the row group's first row is the base of a
+//    descriptor in scalar registers, the row a scalar offset and the lane's
+//    slice a vector offset, so no vector instruction computes an address.
+//    Per row a lane reads one 16-byte piece per 2-bit plane and one 8-byte
+//    piece per 1-bit plane (consecutive lanes on consecutive pieces: every
+//    load instruction reads contiguous bytes), plus the 16-bit scale and zero
+//    point of its slice's group.  Rows go in small batches, the next batches
+//    in flight while one is computed.
+//  * fp16 activations: a code byte v becomes the exact fp16 1024 + v with one
+//    v_perm_b32 and v_dot2_f32_f16 accumulates X.(1024 + v) in fp32; the 1024
+//    and the zero point are removed per (row, slice) with the slice's sum of X:
 //      y += s * (sum_k X_k (1024 + v_k) - (1024 + z - delta) * sum_k X_k)
-//    which equals s * sum_k X_k (v_k + delta - z) (scale and zero point are
-//    shared by the whole 64-code slice because group % 64 == 0);
+//    (scale and zero point are shared by the 64-code slice: group % 64 == 0).
+//    At width 2 under the true prefix, each 2-bit field goes straight to an
+//    exact fp16 2^(10-P) + f with one v_and_or_b32 and a per-position
+//    exponent, and the offsets are removed with a precomputed sum.
 //  * bf16 activations: X is held as fp32 and codes are converted with
-//    v_cvt_f32_ubyte, accumulating with fp32 FMA;
-//  * a lane's per-row partials are summed over the lanes of the row with a
-//    transposing butterfly (each exchange halves the values a lane holds),
-//    then across waves through LDS when a row spans several waves.
+//    v_cvt_f32_ubyte, accumulating with fp32 FMA.
+//  * A lane's per-row partials are summed over the wave with a transposing
+//    butterfly, then across the W waves of a row group through LDS.
+// Each output row is computed by one workgroup in a fixed order, so results
+// do not depend on which calls share a launch.
 #include "mq_common.h"
 #include "mq_kernels.h"
 
 namespace mq {
 
-struct GemvArgs {
-  const void* x;
-  void* y;
-  PlanePtrs pl;
-  const uint16_t* scales;
-  const uint16_t* zeros;
-  int m, n, k, group;
-};
+namespace {
 
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// One call of a launch.  The geometry fields are derived on the host, so the
+// kernel does no integer division.
+struct GemvCall {
+  const uint16_t* x;
+  uint16_t* y;
+  const uint32_t* p[kPlanes];
+  const uint16_t* s;
+  const uint16_t* z;
+  int n, k;
+  int item0;  // first item of the call
+  int wlog;   // log2 of the waves sharing a row (W = 1, 2 or 4)
+  int rpi;    // rows per item: (4 / W) row groups x ROWS
+  int gpr;    // quantization groups per row, k / group
+  int gmul;   // slice -> group index: (slice * gmul) >> 16 == slice / (group / 64)
+};
+
+struct GemvLaunch {
+  GemvCall c[kGemvMaxCalls];
+  int ncalls, m;
+};
+
+// waves that share one row (a lane per 64-code slice): 1, 2 or 4
+__host__ __device__ inline int waves_per_row(int k) {
+  const int w = ((k >> 6) + 63) >> 6;
+  return w >= 3 ? 4 : w;
+}
+
+// Rows per wave: eight, or four for four tokens (the transposing butterfly
+// reduces ROWS x tokens <= 32 values per lane).
+__host__ __device__ constexpr int gemv_rows(int mt) { return mt >= 4 ? 4 : 8; }
 
 // Transposing butterfly stage with xor-offset O on VC values per lane.
 template <int VC, int O>
@@ -82,217 +121,168 @@ __device__ __forceinline__ uint32_t field2_to_f16x2(uint32_t w, uint32_t magic_v
   return r;
 }
 
-// value of quad lane t in every lane of the quad (DPP quad_perm [t,t,t,t]);
-// t is a constant after unrolling
-__device__ __forceinline__ uint32_t quad_bcast(uint32_t v, int t) {
-  switch (t) {
-    case 0: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x00, 0xF, 0xF, false);
-    case 1: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x55, 0xF, 0xF, false);
-    case 2: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xAA, 0xF, 0xF, false);
-    default: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xFF, 0xF, 0xF, false);
-  }
-}
-
 __device__ __forceinline__ float dot2h(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c, false);
 }
 
-// SZ4 (group == 128, even groups per row): the scales and zeros of four rows
-// come in with one dword load per lane (quad lane t fetches the two groups of
-// its quad for row t) and DPP quad broadcasts hand every lane its own value;
-// otherwise each row costs two 16-bit loads per lane.
-// XW = 1: the workgroup's lanes cover one row's slices (several waves when
-// k > 4096) and walk ROWS rows.  XW = 4 (k <= 4096, one wave per row): four
-// waves with ROWS rows each share a workgroup, and the workgroup stages the
-// activations once through LDS instead of every wave reading all of X.
-template <int R, int ROUND, int MT, int BF16, int ROWS, int SZ4, int XW>
-__device__ __forceinline__ void gemv_body(const GemvArgs a, const unsigned blk) {
-  constexpr int NP = planes_needed(R, ROUND);
-  // width 2, true prefix, fp16: fields go straight from the plane-0 word to
-  // fp16 with one and-or per pair (no byte assembly)
-  constexpr bool FAST2 = (R == 2 && !ROUND && !BF16);
-  // rows per load batch: batch b + 1 is in flight while batch b is computed.
-  // Narrow widths carry few bytes per row, so all rows of the block are
-  // requested at once to keep enough bytes in flight; wide ones use small
-  // batches, which shortens the compute tail after the last bytes arrive.
-  constexpr int RB = NP <= 3 ? ROWS : 2;
-  constexpr int NB = ROWS / RB;
+// a value known to be the same in every lane, moved to a scalar register
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Raw buffer descriptor (gfx9 data format word, no stride, 4 GiB - 1 bytes of
+// records) at `base`.  The base is wave-uniform; it is passed through
+// readfirstlane so that the descriptor is built in scalar registers (one the
+// compiler believed divergent would be wrapped in a loop over lanes).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(lo | (hi << 32)), (short)0, -1, 0x00020000);
+}
+// cache-policy operand of the buffer loads: nontemporal (streamed once)
+constexpr int kNontemporal = 2;
+
+template <int R, int ROUND, int MT, int BF16, int ROWS>
+struct GemvWave {
+  static constexpr int NP = planes_needed(R, ROUND);
+  static constexpr bool FAST2 = (R == 2 && !ROUND && !BF16);
+  static constexpr int V = ROWS * MT;
+  // Rows are loaded and computed in batches of RB rows (two for widths of up
+  // to three planes, one for wider ones), PD batches in flight.  Measured on
+  // the 8B FFN shapes against deeper and shallower batches; larger batches
+  // let the compiler convert every staged row before the first dot product
+  // and lower the occupancy.
+  static constexpr int RB = NP <= 3 ? 2 : 1;
+  static constexpr int NB = ROWS / RB;
+  static constexpr int PD = NP == 4 ? 3 : 2;
+  static constexpr float kDelta = ROUND ? 0.0f : prefix_delta(R);
+  static_assert((V & (V - 1)) == 0 && V <= 32, "values per lane must be a power of two");
   static_assert(NB * RB == ROWS, "row batches");
-  constexpr int V = ROWS * MT;
 
-  const int tid = XW > 1 ? (int)(threadIdx.x & 63) : (int)threadIdx.x;  // lane of the row's slices
-  const int lane = tid & 63;
-  const int S = a.k >> 6;
-  const bool valid = tid < S;            // one lane per 64-code slice; a row spans the workgroup
-  const int slice = valid ? tid : 0;
-  const size_t upr = (size_t)(a.k >> 5);  // units per row
-  const int gpr = a.k / a.group;
-  const int gidx = (slice * 64) / a.group;
-  const size_t row0 = ((size_t)blk * XW + (XW > 1 ? (threadIdx.x >> 6) : 0)) * (size_t)ROWS;
+  const GemvCall& C;
+  int wave, lane, wsl, row0, slice, valid;
+  __amdgpu_buffer_rsrc_t rp[NP], rs, rz;
+  int vplane2, vplane1, vgroup;  // per-lane byte offsets
+  uint32_t rec[PD][RB][2][kUnitWords];
+  f16x2_t sz[PD][RB];
+  uint32_t xr[BF16 ? 1 : MT][32];
+  float xf[BF16 ? MT : 1][BF16 ? 64 : 1];
+  float xs[MT], xc[MT];
+  float acc[V];
 
-  // ---- 1. issue the activation loads of this slice ----
-  // (unconditional loads from clamped addresses; invalid lanes/tokens are
-  // zeroed at first use so no load waits behind a branch)
-  uint4 xraw[MT][8];
-  constexpr int XC = XW > 1 ? (MT * 512) / (64 * XW) : 1;  // 16-byte X chunks per thread when staged
-  uint4 xst[XC];
-  if constexpr (XW == 1) {
+  // Row group (wave >> wlog) of the item takes ROWS rows; its W waves split
+  // the row's 64-code slices.
+  __device__ __forceinline__ GemvWave(const GemvCall& call, int it, int w, int l) : C(call), wave(w), lane(l) {
+    wsl = wave & ((1 << C.wlog) - 1);
+    row0 = (it - C.item0) * C.rpi + (wave >> C.wlog) * ROWS;
+    const int sl = (wsl << 6) + lane;
+    valid = sl < (C.k >> 6);
+    slice = valid ? sl : 0;
+    // descriptors based at the row group's first row (clamped to the matrix)
+    const int base = min(row0, C.n - 1);
 #pragma unroll
-    for (int mm = 0; mm < MT; ++mm) {
-      const int mc = mm < a.m ? mm : 0;
-      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + (size_t)mc * a.k +
-                                                        (size_t)slice * 64);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) xraw[mm][i] = src[i];
-    }
-  } else {
-    // chunk c = (token mm, slice sl, piece i) with consecutive threads on
-    // consecutive 16-byte pieces of X; clamped reads for idle slices/tokens
-#pragma unroll
-    for (int j = 0; j < XC; ++j) {
-      const int c = (int)threadIdx.x + 64 * XW * j;
-      const int mm = c >> 9, sl = (c >> 3) & 63, i = c & 7;
-      const int mc = mm < a.m ? mm : 0;
-      const int sc = sl < S ? sl : 0;
-      xst[j] = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + (size_t)mc * a.k +
-                                              (size_t)sc * 64)[i];
-    }
+    for (int p = 0; p < NP; ++p)
+      rp[p] = buffer_rsrc(reinterpret_cast<const char*>(C.p[p]) +
+                          (size_t)base * (size_t)(C.k >> (kPlaneBits[p] == 2 ? 2 : 3)));
+    rs = buffer_rsrc(C.s + (size_t)base * C.gpr);
+    rz = buffer_rsrc(C.z + (size_t)base * C.gpr);
+    vplane2 = slice * 16;
+    vplane1 = slice * 8;
+    vgroup = ((slice * C.gmul) >> 16) * 2;
   }
 
-  // ---- 2. issue the plane loads of the first row batch ----
-  uint32_t rec[2][RB][2][kUnitWords];
-  uint16_t sraw[2][SZ4 ? 1 : RB], zraw[2][SZ4 ? 1 : RB];
-  uint32_t sq[SZ4 ? ROWS / 4 : 1], zq[SZ4 ? ROWS / 4 : 1];  // all rows' quads, loaded once
-  static_assert(!SZ4 || ROWS % 4 == 0, "quad scale loads cover rows in fours");
-  const int qgrp = ((tid >> 6) << 5) + 2 * (lane >> 2);       // first of the quad's two groups
-  const int qgrp_c = qgrp <= gpr - 2 ? qgrp : gpr - 2;          // clamp for idle lanes
-  const int sz_shift = 16 * ((lane >> 1) & 1);                  // this lane's half of the dword
-  auto load_batch = [&](int buf, int b) {
+  // Issue the plane, scale and zero loads of batch b into buffer BUF.  Rows
+  // past n are clamped to n - 1 (their results are not stored).
+  template <int BUF>
+  __device__ __forceinline__ void load_batch(int b) {
+    const int base = min(row0, C.n - 1);
+    const int rb2 = C.k >> 2, rb1 = C.k >> 3;
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
-      size_t row = row0 + (size_t)(b * RB + i);
-      if (row >= (size_t)a.n) row = (size_t)a.n - 1;  // clamp loads; stores are guarded
-      const size_t unit = row * upr + (size_t)slice * 2;
+      const int r = min(row0 + b * RB + i, C.n - 1) - base;  // uniform
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
         if (kPlaneBits[p] == 2) {
-          const stream_u32x4 v = stream_load16(a.pl.p[p] + unit * 2);
-          rec[buf][i][0][kUnitOff[p]] = v.x;
-          rec[buf][i][0][kUnitOff[p] + 1] = v.y;
-          rec[buf][i][1][kUnitOff[p]] = v.z;
-          rec[buf][i][1][kUnitOff[p] + 1] = v.w;
+          const stream_u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rp[p], vplane2, r * rb2, kNontemporal);
+          rec[BUF][i][0][kUnitOff[p]] = v.x;
+          rec[BUF][i][0][kUnitOff[p] + 1] = v.y;
+          rec[BUF][i][1][kUnitOff[p]] = v.z;
+          rec[BUF][i][1][kUnitOff[p] + 1] = v.w;
         } else {
-          const stream_u32x2 v = stream_load8(a.pl.p[p] + unit);
-          rec[buf][i][0][kUnitOff[p]] = v.x;
-          rec[buf][i][1][kUnitOff[p]] = v.y;
+          const stream_u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rp[p], vplane1, r * rb1, kNontemporal);
+          rec[BUF][i][0][kUnitOff[p]] = v.x;
+          rec[BUF][i][1][kUnitOff[p]] = v.y;
         }
       }
-      if constexpr (!SZ4) {
-        sraw[buf][i] = a.scales[row * gpr + gidx];
-        zraw[buf][i] = a.zeros[row * gpr + gidx];
-      }
+      sz[BUF][i].x = __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(rs, vgroup, r * C.gpr * 2, 0));
+      sz[BUF][i].y = __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(rz, vgroup, r * C.gpr * 2, 0));
     }
-  };
-  load_batch(0, 0);
-  if constexpr (SZ4) {
-#pragma unroll
-    for (int q = 0; q < ROWS / 4; ++q) {
-      size_t row = row0 + (size_t)(4 * q + (lane & 3));
-      if (row >= (size_t)a.n) row = (size_t)a.n - 1;
-      sq[q] = *reinterpret_cast<const uint32_t*>(a.scales + row * gpr + qgrp_c);
-      zq[q] = *reinterpret_cast<const uint32_t*>(a.zeros + row * gpr + qgrp_c);
-    }
-  }
-  if constexpr (XW > 1) {
-    // [token][piece][slice]: a wave's reads of one piece are 64 consecutive
-    // 16-byte entries
-    __shared__ uint4 xlds[MT * 8 * 64];
-#pragma unroll
-    for (int j = 0; j < XC; ++j) {
-      const int c = (int)threadIdx.x + 64 * XW * j;
-      xlds[((c >> 9) * 8 + (c & 7)) * 64 + ((c >> 3) & 63)] = xst[j];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int mm = 0; mm < MT; ++mm)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) xraw[mm][i] = xlds[(mm * 8 + i) * 64 + lane];
   }
 
-  // ---- 3. activations: register layout, slice sums ----
-  constexpr uint32_t kOnes = 0x3C003C00u;  // (1.0, 1.0) in fp16
-  uint32_t xr[BF16 ? 1 : MT][32];           // fp16 pairs, natural k order or FAST2 pair order
-  float xf[BF16 ? MT : 1][BF16 ? 64 : 1];
-  float xs[MT];                             // sum of the slice's X
-  float xc[MT];                             // FAST2: sum of X times the fp16 field offsets
+  // Activations of this lane's slice in register form: fp16 pairs (natural
+  // k order, or the field order of the width-2 fast path) or fp32 for bf16,
+  // the slice's sum of X and, for the fast path, the sum of X times the fp16
+  // field offsets.  w[mm] holds the slice's 64 halves of token mm.
+  __device__ __forceinline__ void x_setup(const uint32_t (&w0)[MT][32], int m) {
+    constexpr uint32_t kOnes = 0x3C003C00u;  // (1.0, 1.0) in fp16
 #pragma unroll
-  for (int mm = 0; mm < MT; ++mm) {
-    const uint32_t keep = (valid && mm < a.m) ? 0xFFFFFFFFu : 0u;
-    uint32_t w[32];
+    for (int mm = 0; mm < MT; ++mm) {
+      const uint32_t keep = (valid && mm < m) ? 0xFFFFFFFFu : 0u;
+      uint32_t w[32];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      w[4 * i] = xraw[mm][i].x & keep;
-      w[4 * i + 1] = xraw[mm][i].y & keep;
-      w[4 * i + 2] = xraw[mm][i].z & keep;
-      w[4 * i + 3] = xraw[mm][i].w & keep;
-    }
-    if constexpr (BF16) {
-      float sum = 0.f;
+      for (int i = 0; i < 32; ++i) w[i] = w0[mm][i] & keep;
+      if constexpr (BF16) {
+        float sum = 0.f;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        xf[mm][2 * i] = __builtin_bit_cast(float, w[i] << 16);
-        xf[mm][2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u);
-        sum += xf[mm][2 * i] + xf[mm][2 * i + 1];
-      }
-      xs[mm] = sum;
-    } else {
-      float sum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) sum = dot2h(w[i], kOnes, sum);
-      xs[mm] = sum;
-      if constexpr (FAST2) {
-        // pair idx of plane-0 word (u, d): (b, q) = (idx / 4, idx % 4) holds codes
-        // t0 = 32u + 16d + 4q + b (low half) and t0 + 2 (high half)
-        float c = 0.f;
-#pragma unroll
-        for (int wd = 0; wd < 4; ++wd) {
-#pragma unroll
-          for (int idx = 0; idx < 8; ++idx) {
-            const int b = idx / 4, q = idx % 4;
-            const int t0 = 16 * wd + 4 * q + b;
-            const uint32_t sel = (b == 0) ? 0x05040100u : 0x07060302u;
-            const uint32_t pr = __builtin_amdgcn_perm(w[t0 / 2 + 1], w[t0 / 2], sel);
-            xr[mm][8 * wd + idx] = pr;
-            const int P = 8 * b + 2 * q;
-            const int Pp = (idx < 5) ? P : P - 10;     // field bit after the optional shift by 10
-            const uint32_t off = (uint32_t)(25 - Pp) << 10;  // fp16 2^(10 - Pp)
-            c = dot2h(pr, off | (off << 16), c);
-          }
+        for (int i = 0; i < 32; ++i) {
+          xf[mm][2 * i] = __builtin_bit_cast(float, w[i] << 16);
+          xf[mm][2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u);
+          sum += xf[mm][2 * i] + xf[mm][2 * i + 1];
         }
-        xc[mm] = c;
+        xs[mm] = sum;
       } else {
+        float sum = 0.f;
 #pragma unroll
-        for (int i = 0; i < 32; ++i) xr[mm][i] = w[i];
+        for (int i = 0; i < 32; ++i) sum = dot2h(w[i], kOnes, sum);
+        xs[mm] = sum;
+        if constexpr (FAST2) {
+          // pair idx of plane-0 word (u, d): (b, q) = (idx / 4, idx % 4) holds codes
+          // t0 = 32u + 16d + 4q + b (low half) and t0 + 2 (high half)
+          float cs = 0.f;
+#pragma unroll
+          for (int wd = 0; wd < 4; ++wd) {
+#pragma unroll
+            for (int idx = 0; idx < 8; ++idx) {
+              const int b = idx / 4, q = idx % 4;
+              const int t0 = 16 * wd + 4 * q + b;
+              const uint32_t sel = (b == 0) ? 0x05040100u : 0x07060302u;
+              const uint32_t pr = __builtin_amdgcn_perm(w[t0 / 2 + 1], w[t0 / 2], sel);
+              xr[mm][8 * wd + idx] = pr;
+              const int P = 8 * b + 2 * q;
+              const int Pp = (idx < 5) ? P : P - 10;         // field bit after the optional shift by 10
+              const uint32_t off = (uint32_t)(25 - Pp) << 10;  // fp16 2^(10 - Pp)
+              cs = dot2h(pr, off | (off << 16), cs);
+            }
+          }
+          xc[mm] = cs;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 32; ++i) xr[mm][i] = w[i];
+        }
       }
     }
   }
 
-  float acc[V];
-  constexpr float kDelta = ROUND ? 0.0f : prefix_delta(R);
-  uint32_t mg0 = 0, mg2 = 0, mg4 = 0, mg6 = 0, mg8 = 0;
-  if constexpr (FAST2) {
-    mg0 = vgpr_const<field2_magic<0>()>();
-    mg2 = vgpr_const<field2_magic<2>()>();
-    mg4 = vgpr_const<field2_magic<4>()>();
-    mg6 = vgpr_const<field2_magic<6>()>();
-    mg8 = vgpr_const<field2_magic<8>()>();
-  }
-
-  // ---- 4. rows: batch b computes while batch b+1 is in flight ----
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const int cur = b & 1;
-    if (b + 1 < NB) load_batch(cur ^ 1, b + 1);
+  // dot products of batch b (buffer BUF) into acc
+  template <int BUF>
+  __device__ __forceinline__ void compute_batch(int b) {
+    uint32_t mg0 = 0, mg2 = 0, mg4 = 0, mg6 = 0, mg8 = 0;
+    if constexpr (FAST2) {
+      mg0 = vgpr_const<field2_magic<0>()>();
+      mg2 = vgpr_const<field2_magic<2>()>();
+      mg4 = vgpr_const<field2_magic<4>()>();
+      mg6 = vgpr_const<field2_magic<6>()>();
+      mg8 = vgpr_const<field2_magic<8>()>();
+    }
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
       float dot[MT];
@@ -301,7 +291,7 @@ __device__ __forceinline__ void gemv_body(const GemvArgs a, const unsigned blk) 
       if constexpr (FAST2) {
 #pragma unroll
         for (int wd = 0; wd < 4; ++wd) {
-          const uint32_t w = rec[cur][i][wd / 2][kUnitOff[0] + (wd & 1)];
+          const uint32_t w = rec[BUF][i][wd / 2][kUnitOff[0] + (wd & 1)];
           const uint32_t ws = w >> 10;
           uint32_t h[8];
           h[0] = field2_to_f16x2<0>(w, mg0);
@@ -321,14 +311,14 @@ __device__ __forceinline__ void gemv_body(const GemvArgs a, const unsigned blk) 
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           uint32_t bytes[8];
-          bytes[0] = assemble_word<NP, 0>(rec[cur][i][u]);
-          bytes[1] = assemble_word<NP, 1>(rec[cur][i][u]);
-          bytes[2] = assemble_word<NP, 2>(rec[cur][i][u]);
-          bytes[3] = assemble_word<NP, 3>(rec[cur][i][u]);
-          bytes[4] = assemble_word<NP, 4>(rec[cur][i][u]);
-          bytes[5] = assemble_word<NP, 5>(rec[cur][i][u]);
-          bytes[6] = assemble_word<NP, 6>(rec[cur][i][u]);
-          bytes[7] = assemble_word<NP, 7>(rec[cur][i][u]);
+          bytes[0] = assemble_word<NP, 0>(rec[BUF][i][u]);
+          bytes[1] = assemble_word<NP, 1>(rec[BUF][i][u]);
+          bytes[2] = assemble_word<NP, 2>(rec[BUF][i][u]);
+          bytes[3] = assemble_word<NP, 3>(rec[BUF][i][u]);
+          bytes[4] = assemble_word<NP, 4>(rec[BUF][i][u]);
+          bytes[5] = assemble_word<NP, 5>(rec[BUF][i][u]);
+          bytes[6] = assemble_word<NP, 6>(rec[BUF][i][u]);
+          bytes[7] = assemble_word<NP, 7>(rec[BUF][i][u]);
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             if constexpr (BF16) {
@@ -359,17 +349,8 @@ __device__ __forceinline__ void gemv_body(const GemvArgs a, const unsigned blk) 
           }
         }
       }
-      float s, z;
-      if constexpr (SZ4) {
-        const int ri = b * RB + i;  // row within the workgroup's block
-        const uint32_t sd = quad_bcast(sq[ri / 4], ri % 4);
-        const uint32_t zd = quad_bcast(zq[ri / 4], ri % 4);
-        s = h2f((uint16_t)(sd >> sz_shift));
-        z = h2f((uint16_t)(zd >> sz_shift));
-      } else {
-        s = h2f(sraw[cur][i]);
-        z = h2f(zraw[cur][i]);
-      }
+      const float s = (float)sz[BUF][i].x;
+      const float z = (float)sz[BUF][i].y;
 #pragma unroll
       for (int mm = 0; mm < MT; ++mm) {
         float t;
@@ -386,120 +367,154 @@ __device__ __forceinline__ void gemv_body(const GemvArgs a, const unsigned blk) 
     }
   }
 
-  // ---- transposing butterfly over the 64 lanes of the wave ----
-  // Stage o (32, 16, ...) halves the values a lane holds: the lower lane of
-  // each pair keeps the first half and the upper lane the second half, each
-  // adding its partner's copy.  After log2(V) stages lane l holds the sum of
-  // value (l >> (6 - log2 V)) over the lanes that share its upper bits; the
-  // remaining stages are plain xor-reductions.
-  constexpr int T = (V >= 32) ? 5 : (V >= 16) ? 4 : (V >= 8) ? 3 : (V >= 4) ? 2 : (V >= 2) ? 1 : 0;
-  static_assert((1 << T) == V, "values per lane must be a power of two");
-  butterfly<V, 32>(acc, lane);
-  const int idx = lane >> (6 - T);
-  const bool holder = (lane & ((1 << (6 - T)) - 1)) == 0;
-
-  auto store = [&](int id, float val) {
-    const int i = id / MT, mm = id % MT;
-    const size_t row = row0 + (size_t)i;
-    if (row < (size_t)a.n && mm < a.m) {
-      uint16_t* y = static_cast<uint16_t*>(a.y) + (size_t)mm * a.n + row;
-      if constexpr (BF16) *y = (uint16_t)(pack_bf16x2(val, 0.f) & 0xFFFFu);
-      else *y = (uint16_t)(pack_f16x2(val, 0.f) & 0xFFFFu);
-    }
-  };
-
-  const int nwaves = blockDim.x >> 6;
-  if (XW > 1 || nwaves == 1) {
-    if (holder) store(idx, acc[0]);
-  } else {
-    // a row spans several waves: combine the per-wave sums through LDS
-    extern __shared__ float red[];  // [waves][V]
-    const int wave = tid >> 6;
-    if (holder) red[wave * V + idx] = acc[0];
-    __syncthreads();
-    if (tid < V) {
-      float t = 0.f;
-      for (int w = 0; w < nwaves; ++w) t += red[w * V + tid];
-      store(tid, t);
+  // the first PD batches
+  template <int B>
+  __device__ __forceinline__ void issue() {
+    if constexpr (B < PD) {
+      load_batch<B>(B);
+      issue<B + 1>();
     }
   }
-}
+  // batch B computes from buffer B % PD, which then takes batch B + PD
+  template <int B>
+  __device__ __forceinline__ void run() {
+    if constexpr (B < NB) {
+      compute_batch<B % PD>(B);
+      if constexpr (B + PD < NB) load_batch<B % PD>(B + PD);
+      run<B + 1>();
+    }
+  }
 
-template <int R, int ROUND, int MT, int BF16, int ROWS, int SZ4, int XW>
-__global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
-  gemv_body<R, ROUND, MT, BF16, ROWS, SZ4, XW>(a, blockIdx.x);
-}
-
-// Several independent calls of one shape class (same m, k, width, rule,
-// group, dtype) in one launch: workgroup b serves the call whose block range
-// holds b.  One launch then streams the bytes of all of them, so the launch
-// ramp and drain are paid once.
-struct GemvBatch {
-  GemvArgs call[kGemvMaxBatch];
-  int first_block[kGemvMaxBatch];  // first workgroup of each call
-  int ncalls;
+  // Sum acc over the wave (and the row group's waves through `red`) and
+  // store the row results.
+  __device__ __forceinline__ void finish(float* red, int m) {
+    // after log2(V) butterfly stages lane l holds the sum of value
+    // l >> (6 - log2 V) over the lanes that share its upper bits
+    constexpr int T = (V >= 32) ? 5 : (V >= 16) ? 4 : (V >= 8) ? 3 : (V >= 4) ? 2 : (V >= 2) ? 1 : 0;
+    butterfly<V, 32>(acc, lane);
+    const int idx = lane >> (6 - T);
+    const bool holder = (lane & ((1 << (6 - T)) - 1)) == 0;
+    auto store = [&](int id, float val) {
+      const int row = row0 + id / MT, mm = id % MT;
+      if (row < C.n && mm < m) {
+        uint16_t* y = C.y + (size_t)mm * C.n + row;
+        if constexpr (BF16) *y = (uint16_t)(pack_bf16x2(val, 0.f) & 0xFFFFu);
+        else *y = (uint16_t)(pack_f16x2(val, 0.f) & 0xFFFFu);
+      }
+    };
+    if (C.wlog == 0) {
+      if (holder) store(idx, acc[0]);
+    } else {
+      if (holder) red[wave * V + idx] = acc[0];
+      __syncthreads();
+      if (wsl == 0 && lane < V) {
+        float t = 0.f;
+        for (int w = 0; w < (1 << C.wlog); ++w) t += red[(wave + w) * V + lane];
+        store(lane, t);
+      }
+    }
+  }
 };
 
-template <int R, int ROUND, int MT, int BF16, int ROWS, int SZ4, int XW>
-__global__ __launch_bounds__(256) void gemv_batch_kernel(GemvBatch b) {
+// One workgroup per item: the item's call is found by a scalar search of the
+// kernel arguments.  A row group of one wave (k <= 4096) shares the
+// activations of its call with the other three waves through LDS; wider rows
+// split the slices over 2 or 4 waves and each lane loads its own.
+template <int R, int ROUND, int MT, int BF16, int ROWS>
+__global__ __launch_bounds__(256) void gemv_multi_kernel(GemvLaunch a) {
+  using Wave = GemvWave<R, ROUND, MT, BF16, ROWS>;
+  __shared__ float red[4 * Wave::V];
+  __shared__ uint4 xlds[MT * 8 * 64];  // [token][piece][slice] for one-wave rows
+  const int it = (int)blockIdx.x;
   int c = 0;
+  while (c + 1 < a.ncalls && it >= a.c[c + 1].item0) ++c;
+  const GemvCall& C = a.c[c];
+  const int wave = uniform((int)(threadIdx.x >> 6));
+  const int lane = (int)(threadIdx.x & 63);
+  Wave w(C, it, wave, lane);
+  // the weight loads go out first; the activations are read while they fly
+  w.template issue<0>();
+  uint32_t xw[MT][32];
+  if (C.wlog == 0) {
+    // chunk j of thread t: piece (t + 256 j) of the [token][slice][piece] X
+    // block (16-byte pieces, consecutive threads on consecutive pieces)
+    constexpr int XC = (MT * 512) / 256;
+    const int S = C.k >> 6;
 #pragma unroll
-  for (int i = 1; i < kGemvMaxBatch; ++i)
-    if (i < b.ncalls && (int)blockIdx.x >= b.first_block[i]) c = i;
-  gemv_body<R, ROUND, MT, BF16, ROWS, SZ4, XW>(b.call[c], blockIdx.x - (unsigned)b.first_block[c]);
+    for (int j = 0; j < XC; ++j) {
+      const int cidx = (int)threadIdx.x + 256 * j;
+      const int mm = cidx >> 9, sl = (cidx >> 3) & 63, i = cidx & 7;
+      const int mc = mm < a.m ? mm : 0;
+      const int sc = sl < S ? sl : 0;
+      xlds[((cidx >> 9) * 8 + (cidx & 7)) * 64 + ((cidx >> 3) & 63)] =
+          reinterpret_cast<const uint4*>(C.x + (size_t)mc * C.k + (size_t)sc * 64)[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int mm = 0; mm < MT; ++mm)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint4 v = xlds[(mm * 8 + i) * 64 + lane];
+        xw[mm][4 * i] = v.x;
+        xw[mm][4 * i + 1] = v.y;
+        xw[mm][4 * i + 2] = v.z;
+        xw[mm][4 * i + 3] = v.w;
+      }
+  } else {
+#pragma unroll
+    for (int mm = 0; mm < MT; ++mm) {
+      const int mc = mm < a.m ? mm : 0;
+      const uint4* src = reinterpret_cast<const uint4*>(C.x + (size_t)mc * C.k + (size_t)w.slice * 64);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint4 v = src[i];
+        xw[mm][4 * i] = v.x;
+        xw[mm][4 * i + 1] = v.y;
+        xw[mm][4 * i + 2] = v.z;
+        xw[mm][4 * i + 3] = v.w;
+      }
+    }
+  }
+  w.x_setup(xw, a.m);
+  w.template run<0>();
+  w.finish(red, a.m);
 }
 
-template <int R, int ROUND, int MT, int BF16, int SZ4, int XW, int ROWS>
-static void gemv_launch_k(const GemvBatch& b, int ncalls, unsigned blocks, int threads, size_t lds, hipStream_t s) {
-  if (ncalls == 1)
-    hipLaunchKernelGGL((gemv_kernel<R, ROUND, MT, BF16, ROWS, SZ4, XW>), dim3(blocks), dim3(threads), lds, s, b.call[0]);
-  else
-    hipLaunchKernelGGL((gemv_batch_kernel<R, ROUND, MT, BF16, ROWS, SZ4, XW>), dim3(blocks), dim3(threads), lds, s, b);
-}
+int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 
 template <int R, int ROUND, int MT, int BF16>
-static hipError_t gemv_launch_t(const LinearArgs* la, int ncalls, hipStream_t s) {
-  constexpr int ROWS = (MT >= 4) ? 4 : 8;
-  // every call of a batch shares k and group, hence the workgroup shape
-  const int S = la[0].k / 64;
-  const int xw = S <= 64 ? 4 : 1;  // four row groups share the staged X when a row fits one wave
-  GemvBatch b;
-  unsigned blocks = 0;
+hipError_t gemv_launch_t(const LinearArgs* la, int ncalls, hipStream_t s) {
+  constexpr int ROWS = gemv_rows(MT);
+  GemvLaunch a;
+  int items = 0;
   for (int i = 0; i < ncalls; ++i) {
-    GemvArgs& a = b.call[i];
-    a.x = la[i].x;
-    a.y = la[i].y;
-    a.pl = la[i].pl;
-    a.scales = la[i].scales;
-    a.zeros = la[i].zeros;
-    a.m = la[i].m;
-    a.n = la[i].n;
-    a.k = la[i].k;
-    a.group = la[i].group;
-    b.first_block[i] = (int)blocks;
-    blocks += (unsigned)((la[i].n + xw * ROWS - 1) / (xw * ROWS));
+    GemvCall& c = a.c[i];
+    c.x = static_cast<const uint16_t*>(la[i].x);
+    c.y = static_cast<uint16_t*>(la[i].y);
+    for (int p = 0; p < kPlanes; ++p) c.p[p] = la[i].pl.p[p];
+    c.s = la[i].scales;
+    c.z = la[i].zeros;
+    c.n = la[i].n;
+    c.k = la[i].k;
+    c.item0 = items;
+    const int W = waves_per_row(la[i].k);
+    c.wlog = W == 1 ? 0 : W == 2 ? 1 : 2;
+    c.rpi = (4 / W) * ROWS;
+    c.gpr = la[i].k / la[i].group;
+    // exact for slice < 256 and group / 64 <= 256: the rounding error of the
+    // multiplier stays below 1 / (group / 64)
+    c.gmul = (65536 + la[i].group / 64 - 1) / (la[i].group / 64);
+    items += cdiv(la[i].n, c.rpi);
   }
-  for (int i = ncalls; i < kGemvMaxBatch; ++i) {
-    b.call[i] = b.call[0];
-    b.first_block[i] = (int)blocks;
-  }
-  b.ncalls = ncalls;
-  const int gpr = la[0].k / la[0].group;
-  const bool sz4 = la[0].group == 128 && gpr % 2 == 0;
-  if (xw == 4) {
-    if (sz4) gemv_launch_k<R, ROUND, MT, BF16, 1, 4, ROWS>(b, ncalls, blocks, 256, 0, s);
-    else gemv_launch_k<R, ROUND, MT, BF16, 0, 4, ROWS>(b, ncalls, blocks, 256, 0, s);
-  } else {
-    const int threads = ((S + 63) / 64) * 64;  // one lane per 64-code slice, whole waves
-    const size_t lds = (size_t)(threads / 64) * ROWS * MT * sizeof(float);
-    if (sz4) gemv_launch_k<R, ROUND, MT, BF16, 1, 1, ROWS>(b, ncalls, blocks, threads, lds, s);
-    else gemv_launch_k<R, ROUND, MT, BF16, 0, 1, ROWS>(b, ncalls, blocks, threads, lds, s);
-  }
+  for (int i = ncalls; i < kGemvMaxCalls; ++i) a.c[i] = a.c[ncalls - 1];
+  a.ncalls = ncalls;
+  a.m = la[0].m;
+  hipLaunchKernelGGL((gemv_multi_kernel<R, ROUND, MT, BF16, ROWS>), dim3((unsigned)items), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 template <int R, int ROUND, int BF16>
-static hipError_t gemv_launch_m(const LinearArgs* a, int n, hipStream_t s) {
+hipError_t gemv_launch_m(const LinearArgs* a, int n, hipStream_t s) {
   if constexpr (BF16) {
     return gemv_launch_t<R, ROUND, 1, 1>(a, n, s);  // bf16: m == 1 only
   } else {
@@ -512,12 +527,14 @@ static hipError_t gemv_launch_m(const LinearArgs* a, int n, hipStream_t s) {
 }
 
 template <int R, int ROUND>
-static hipError_t gemv_launch_d(const LinearArgs* a, int n, hipStream_t s) {
+hipError_t gemv_launch_d(const LinearArgs* a, int n, hipStream_t s) {
   return a[0].bf16 ? gemv_launch_m<R, ROUND, 1>(a, n, s) : gemv_launch_m<R, ROUND, 0>(a, n, s);
 }
 
-hipError_t launch_gemv_batch(const LinearArgs* a, int ncalls, hipStream_t s) {
-  if (ncalls < 1 || ncalls > kGemvMaxBatch) return hipErrorInvalidValue;
+}  // namespace
+
+hipError_t launch_gemv_multi(const LinearArgs* a, int ncalls, hipStream_t s) {
+  if (ncalls < 1 || ncalls > kGemvMaxCalls) return hipErrorInvalidValue;
 #define MQ_GEMV_CASE(RR) \
   case RR: return a[0].round_rule ? gemv_launch_d<RR, 1>(a, ncalls, s) : gemv_launch_d<RR, 0>(a, ncalls, s);
   switch (a[0].r) {
@@ -530,7 +547,5 @@ hipError_t launch_gemv_batch(const LinearArgs* a, int ncalls, hipStream_t s) {
   }
 #undef MQ_GEMV_CASE
 }
-
-hipError_t launch_gemv(const LinearArgs& a, hipStream_t s) { return launch_gemv_batch(&a, 1, s); }
 
 }  // namespace mq

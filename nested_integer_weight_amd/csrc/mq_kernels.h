@@ -35,12 +35,11 @@ constexpr int kGemvMaxK = 16384;
 __host__ inline bool gemv_eligible(int m, int k, int bf16) {
   return m >= 1 && k <= kGemvMaxK && (bf16 ? m == 1 : m <= kGemvMaxM);
 }
-hipError_t launch_gemv(const LinearArgs& a, hipStream_t s);
-// up to kGemvMaxBatch independent GEMV-eligible calls that share m, k, width,
-// rule, group and dtype, in one launch (no call may read or write another's
-// output)
-constexpr int kGemvMaxBatch = 4;
-hipError_t launch_gemv_batch(const LinearArgs* a, int ncalls, hipStream_t s);
+// Up to kGemvMaxCalls independent GEMV-eligible calls that share m, width,
+// rule and dtype (any n, k, group) in one launch.  No call may write what
+// another call of the launch reads or writes.
+constexpr int kGemvMaxCalls = 32;
+hipError_t launch_gemv_multi(const LinearArgs* a, int ncalls, hipStream_t s);
 
 // MFMA skinny path (weights dequantized straight into MFMA operand registers,
 // activations shared through LDS): 2 <= m <= 64 with k a multiple of 256.

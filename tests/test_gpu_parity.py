@@ -268,9 +268,9 @@ def test_mixed_equals_single_calls(mq):
 @pytest.mark.parametrize("m,dt,r,rule,group", [(1, "f16", 2, O.PREFIX, 128), (3, "f16", 3, O.ROUND, 64),
                                                 (1, "bf16", 8, O.PREFIX, 128), (2, "f16", 6, O.PREFIX, 256)])
 def test_mixed_batches_independent_gemv_calls(mq, m, dt, r, rule, group):
-    # five independent calls of one shape class with ragged n: the library runs
-    # the first four in one launch and the fifth alone; each result must equal
-    # its single call bit for bit and the oracle within tolerance
+    # five independent calls of one shape class with ragged n in one launch;
+    # each result must equal its single call bit for bit and the oracle within
+    # tolerance
     calls, lays = [], []
     for i, n in enumerate((1, 70, 333, 8, 1025)):
         lay = synth.make_layer(cfg_id=5, tensor_id=300 + 10 * i + r, n=n, k=1024, m=m, group=group, x_dtype=dt)
@@ -283,6 +283,60 @@ def test_mixed_batches_independent_gemv_calls(mq, m, dt, r, rule, group):
         single = mq.linear(c.x, c.packed, c.r, c.rule, c.group, c.scales, c.zeros)
         assert torch.equal(single, y)
         check_y(y, lay, lay.x, c.r, c.rule)
+
+
+@pytest.mark.parametrize("r,rule,dt", [(2, O.PREFIX, "f16"), (3, O.ROUND, "f16"), (8, O.PREFIX, "bf16"),
+                                       (6, O.ROUND, "bf16")])
+def test_mixed_heterogeneous_gemv_launch(mq, r, rule, dt):
+    # one width class, calls of every row-group layout (k <= 4096: one wave per
+    # row; 4096 < k <= 8192: two; larger: four) and of several groups, with a
+    # skinny call and a call of another width in between: every result equals
+    # its single call bit for bit and the oracle within tolerance
+    specs = [(1, 300, 4096, 128), (1, 77, 14336, 128), (1, 130, 6144, 64), (8, 96, 1024, 128),
+             (1, 64, 3584, 256), (1, 512, 256, 64), (1, 33, 16384, 128), (1, 40, 12288, 512)]
+    calls, lays = [], []
+    for i, (m, n, k, g) in enumerate(specs):
+        lay = synth.make_layer(cfg_id=9, tensor_id=10 * i + r, n=n, k=k, m=m, group=g, x_dtype=dt)
+        q, s, z = to_dev(lay)
+        rr = 4 if i == 4 else r  # one call of another width
+        calls.append(mq.Call(x=lay.x.to(DEV), packed=mq.pack_parent(q).truncated(rr, rule), r=rr, rule=rule,
+                             group=g, scales=s, zeros=z))
+        lays.append(lay)
+    outs = mq.linear_mixed(calls)
+    for c, lay, y in zip(calls, lays, outs):
+        single = mq.linear(c.x, c.packed, c.r, c.rule, c.group, c.scales, c.zeros)
+        assert torch.equal(single, y)
+        check_y(y, lay, lay.x, c.r, c.rule)
+
+
+def test_mixed_hazards_beyond_activations(mq):
+    # a call whose output is another call's scale array must run before that
+    # call reads it, and after an earlier call that reads the old scales
+    k = 512
+    lays = [synth.make_layer(cfg_id=9, tensor_id=200 + i, n=256, k=k, m=1, group=128, x_dtype="f16")
+            for i in range(3)]
+    dev = [to_dev(l) for l in lays]
+    packs = [mq.pack_parent(q) for q, _, _ in dev]
+    xs = [l.x.to(DEV) for l in lays]
+    shared_s = dev[1][1].clone()  # [256, 4] fp16 = 2 KB, written by call 1 below
+    y_a = torch.empty((1, 256), dtype=torch.float16, device=DEV)
+    y_c = torch.empty((1, 256), dtype=torch.float16, device=DEV)
+    y_b = shared_s.view(-1)[:256].view(1, 256)  # call B writes into the scales call C reads
+
+    def calls():
+        return [mq.Call(x=xs[0], packed=packs[0], r=4, rule=O.PREFIX, group=128, scales=shared_s,
+                        zeros=dev[0][2], out=y_a),          # A reads shared_s (before B writes it)
+                mq.Call(x=xs[1], packed=packs[1], r=4, rule=O.PREFIX, group=128, scales=dev[1][1],
+                        zeros=dev[1][2], out=y_b),          # B writes into shared_s
+                mq.Call(x=xs[2], packed=packs[2], r=4, rule=O.PREFIX, group=128, scales=shared_s,
+                        zeros=dev[2][2], out=y_c)]          # C reads shared_s after B
+    init = shared_s.clone()
+    mq.linear_mixed(calls())
+    got = (y_a.clone(), shared_s.clone(), y_c.clone())
+    shared_s.copy_(init)
+    for c in calls():
+        mq.linear(c.x, c.packed, c.r, c.rule, c.group, c.scales, c.zeros, out=c.out)
+    assert torch.equal(got[0], y_a) and torch.equal(got[1], shared_s) and torch.equal(got[2], y_c)
 
 
 def test_mixed_dependent_gemv_calls_keep_order(mq):
