@@ -155,6 +155,26 @@ mq_status mq_linear(const void* x, int32_t x_dtype, int32_t m, const mq_packed* 
                     int32_t rule, int32_t group, const uint16_t* scales, const uint16_t* zeros,
                     void* y, void* workspace, size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): mq_linear
+ * with the split-k workspace taken from a static array in the library
+ * instead of a caller argument.  Calls no hipMalloc, hipFree or allocating
+ * routine.  The array is MQ_NOALLOC_SCRATCH_BYTES per device, held from the
+ * library's load until the process ends; its address is looked up once per
+ * device on the first call there.  Returns MQ_ESIZE when the shape needs more
+ * split-k workspace than that (mq_linear_workspace_bytes(m, n, k) >
+ * MQ_NOALLOC_SCRATCH_BYTES), and MQ_EINVAL when `stream` does not belong to
+ * the current device.  Every call on a device shares that device's array:
+ * calls that overlap in time on one device (different streams, or different
+ * threads on unordered streams) race and must be ordered by the caller.  The
+ * array keeps the last call's partial sums; every call overwrites the part it
+ * reads.  Results are those of mq_linear with a workspace of
+ * MQ_NOALLOC_SCRATCH_BYTES bytes, bit for bit. */
+#define MQ_NOALLOC_SCRATCH_BYTES (64u << 20)
+mq_status mq_linear_noalloc(const void* x, int32_t x_dtype, int32_t m, const mq_packed* w, int32_t r,
+                            int32_t rule, int32_t group, const uint16_t* scales, const uint16_t* zeros, void* y,
+                            void* stream);
+
 /* Mix'n'Match ("Matryoshka Quantization | Summary", section 4.3): n_calls
  * layer matrices, each at its own width, issued on one stream and sharing one
  * workspace.  All calls are validated before the first launch; an invalid call

@@ -23,8 +23,12 @@ STATUS = {
 # every symbol include/mq.h declares
 EXPORTS = (
     "mq_status_str", "mq_plane_bytes", "mq_planes_needed", "mq_pack_parent",
-    "mq_linear_workspace_bytes", "mq_linear", "mq_linear_mixed", "mq_slice_codes", "mq_dequant",
+    "mq_linear_workspace_bytes", "mq_linear", "mq_linear_noalloc", "mq_linear_mixed", "mq_slice_codes",
+    "mq_dequant",
 )
+
+# bytes of the static split-k scratch behind mq_linear_noalloc (MQ_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class MqPacked(ctypes.Structure):
@@ -71,6 +75,8 @@ def lib() -> ctypes.CDLL:
     L.mq_linear_workspace_bytes.restype = sz
     L.mq_linear.argtypes = [vp, i32, i32, P, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     L.mq_linear.restype = ctypes.c_int
+    L.mq_linear_noalloc.argtypes = [vp, i32, i32, P, i32, i32, i32, vp, vp, vp, vp]
+    L.mq_linear_noalloc.restype = ctypes.c_int
     L.mq_linear_mixed.argtypes = [ctypes.POINTER(MqCall), i32, vp, sz, ctypes.POINTER(i32), vp]
     L.mq_linear_mixed.restype = ctypes.c_int
     L.mq_slice_codes.argtypes = [P, i32, i32, vp, vp]

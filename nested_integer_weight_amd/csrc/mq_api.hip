@@ -1,6 +1,9 @@
 // mq_api.hip -- the C ABI declared in include/mq.h: host-side validation,
-// kernel choice, launches.  No memory is allocated and no state is kept.
+// kernel choice, launches.  No memory is allocated; the only state is the
+// per-device address of the static scratch array of mq_linear_noalloc.
 #include <stdint.h>
+
+#include <atomic>
 
 #include "../../include/mq.h"
 #include "mq_kernels.h"
@@ -157,6 +160,33 @@ PlanePtrs planes_of(const mq_call& c) {
 // calls looked at together when forming launches
 constexpr int kWindow = 256;
 
+// ---------------------------------------------------------------------------
+// Scratch for mq_linear_noalloc: the split-k partial sums of callers that
+// cannot allocate.  Every device the library runs on holds its own copy until
+// the process ends.  Host code never uses the array's name as an address: the
+// device address comes from hipGetSymbolAddress, once per device.
+// ---------------------------------------------------------------------------
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[MQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// Device address of `scratch` on device dev, which must be the current device.
+mq_status scratch_on(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return MQ_EINVAL;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MQ_EHIP;
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return MQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -218,6 +248,25 @@ mq_status mq_linear(const void* x, int32_t x_dtype, int32_t m, const mq_packed* 
   mq_status st = validate_linear(x, x_dtype, m, w, r, rule, group, scales, zeros, y, &pl);
   if (st != MQ_OK) return st;
   return run_linear(x, x_dtype, m, w, r, rule, group, scales, zeros, y, workspace, workspace_bytes, pl,
+                    static_cast<hipStream_t>(stream));
+}
+
+mq_status mq_linear_noalloc(const void* x, int32_t x_dtype, int32_t m, const mq_packed* w, int32_t r,
+                            int32_t rule, int32_t group, const uint16_t* scales, const uint16_t* zeros, void* y,
+                            void* stream) {
+  PlanePtrs pl;
+  mq_status st = validate_linear(x, x_dtype, m, w, r, rule, group, scales, zeros, y, &pl);
+  if (st != MQ_OK) return st;
+  if (m == 0) return MQ_OK;
+  if (mq_linear_workspace_bytes(m, w->n, w->k) > (size_t)MQ_NOALLOC_SCRATCH_BYTES) return MQ_ESIZE;
+  int dev = -1, sdev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MQ_EHIP;
+  if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev) != hipSuccess) return MQ_EHIP;
+  if (sdev != dev) return MQ_EINVAL;
+  void* ws = nullptr;
+  st = scratch_on(dev, &ws);
+  if (st != MQ_OK) return st;
+  return run_linear(x, x_dtype, m, w, r, rule, group, scales, zeros, y, ws, (size_t)MQ_NOALLOC_SCRATCH_BYTES, pl,
                     static_cast<hipStream_t>(stream));
 }
 

@@ -151,6 +151,21 @@ def linear(x: torch.Tensor, packed: Packed, r: int, rule, group: int, scales: to
     return y
 
 
+def linear_noalloc(x: torch.Tensor, packed: Packed, r: int, rule, group: int, scales: torch.Tensor,
+                   zeros: torch.Tensor, out: torch.Tensor) -> torch.Tensor:
+    """linear() with the split-k workspace taken from the library's static
+    per-device scratch (no device allocation by the library; `out` is the
+    caller's).  Calls that overlap in time on one device share the scratch."""
+    _check_layer_args(x, packed, scales, zeros, group)
+    _need_cuda(out, "out", x.dtype)
+    if out.shape != (x.shape[0], packed.n):
+        raise ValueError(f"out must be [{x.shape[0]}, {packed.n}]")
+    _lib.check(_lib.lib().mq_linear_noalloc(_ptr(x), _DTYPES[x.dtype], x.shape[0], ctypes.byref(packed.cstruct()), r,
+                                            RULES[rule], group, _ptr(scales), _ptr(zeros), _ptr(out),
+                                            _stream(x.device)), "mq_linear_noalloc")
+    return out
+
+
 @dataclass
 class Call:
     x: torch.Tensor

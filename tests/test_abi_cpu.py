@@ -132,3 +132,20 @@ def test_workspace_query_is_pure(L):
     assert L.mq_linear_workspace_bytes(0, 14336, 4096) == 0
     ws = L.mq_linear_workspace_bytes(64, 4096, 14336)
     assert ws % (64 * 4096 * 4) == 0
+
+
+def test_noalloc_validation_before_any_hip_call(L):
+    w = _packed(n=6144, k=14336)
+    args = dict(x=4096, dt=2, s=4096, z=8192, y=12288)
+    # invalid arguments are rejected exactly as by mq_linear
+    assert L.mq_linear_noalloc(args["x"], 2, 1, ctypes.byref(w), 5, 0, 128, args["s"], args["z"], args["y"],
+                               None) == 2
+    assert L.mq_linear_noalloc(args["x"], 2, 1, ctypes.byref(w), 4, 0, 96, args["s"], args["z"], args["y"],
+                               None) == 3
+    # m = 0 is a no-op
+    assert L.mq_linear_noalloc(args["x"], 2, 0, ctypes.byref(w), 4, 0, 128, args["s"], args["z"], args["y"],
+                               None) == 0
+    # a shape whose split-k workspace exceeds the static scratch is refused
+    assert L.mq_linear_workspace_bytes(2048, 6144, 14336) > _lib.NOALLOC_SCRATCH_BYTES
+    assert L.mq_linear_noalloc(args["x"], 2, 2048, ctypes.byref(w), 4, 0, 128, args["s"], args["z"], args["y"],
+                               None) == 9
