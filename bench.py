@@ -24,6 +24,9 @@ stream bracket the replays.
                the two launches a dependent FFN block needs (gate+up, then
                down reading their product), each averaged over >= 200 launches.
   roofline     the launch with the most time per step (r = 8).
+  attention    the Llama-3.1-8B attention projections (q, o 4096->4096; k, v
+               4096->1024) at M = 1 (one launch per width, and the q/k/v then
+               o launches of a dependent block) and M = 16, 64.
   prefill      the M = 2048 bf16 GEMM (same shapes, r in {2, 4, 8}).
   skinny       decode batches M in {8, 16, 32, 64} at r in {2, 3, 4, 8}
                against max(HBM time, MFMA time).
@@ -98,6 +101,7 @@ def main():
     ap.add_argument("--no-skinny", action="store_true", help="skip the M in {8,16,32,64} lines")
     ap.add_argument("--no-mix", action="store_true", help="skip the 42-block Mix'n'Match stack lines")
     ap.add_argument("--no-pieces", action="store_true", help="skip the per-launch figures")
+    ap.add_argument("--no-attn", action="store_true", help="skip the attention-projection lines")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -285,6 +289,77 @@ def main():
                               "(4096x14336) in one launch (mq_linear_mixed decode path)",
                     "bytes_per_launch": dom["bytes_per_launch"], "us_per_launch": dom["us_per_launch"]}
 
+    # ---------------- attention projections (Llama-3.1-8B q, k, v, o) ----------------
+    # Decode at M = 1: the four projections of a width in one launch (each reads
+    # a fixed input, as the FFN calls do), and the two launches a dependent
+    # attention block needs (q, k and v, then o); M = 16 and 64 through the
+    # skinny path.  Own ring: its smallest piece is ~10 MB.
+    attn = None
+    if not args.no_attn:
+        attn = {}
+        amin = sum(alg_bytes(1, n, k, 2) for _, n, k in synth.LLAMA8B_ATTN)
+        aring = math.ceil(RING_BYTES / amin)
+        amats = []
+        for tid, (name, n, k) in enumerate(synth.LLAMA8B_ATTN):
+            lay = synth.make_layer(cfg_id=12, tensor_id=tid, n=n, k=k, m=0, group=GROUP, outlier_frac=1e-3)
+            q = torch.from_numpy(lay.q).to(dev)
+            s = torch.from_numpy(lay.scales).to(dev)
+            z = torch.from_numpy(lay.zeros).to(dev)
+            base = mq.pack_parent(q)
+            copies = [(mq.Packed(n, k, [p.clone() for p in base.planes]), s.clone(), z.clone())
+                      for _ in range(aring)]
+            del q, base
+            xa = {m: synth.activations(synth.rng_for(12, 200 + tid, m), m, k, "f16").to(dev) for m in (1, 16, 64)}
+            ya = {m: torch.empty((m, n), dtype=torch.float16, device=dev) for m in (1, 16, 64)}
+            amats.append(dict(name=name, n=n, k=k, copies=copies, x=xa, y=ya))
+        torch.cuda.synchronize()
+        log(f"[bench] attention: 4 parents, {aring} copies")
+
+        def attn_calls(i, r, m, idx=(0, 1, 2, 3)):
+            c = i % aring
+            return [mq.Call(x=amats[j]["x"][m], packed=amats[j]["copies"][c][0].truncated(r), r=r, rule="prefix",
+                            group=GROUP, scales=amats[j]["copies"][c][1], zeros=amats[j]["copies"][c][2],
+                            out=amats[j]["y"][m]) for j in idx]
+
+        def apiece(fn, nbytes, nflop=0.0):
+            fn(0)  # eager first: any workspace is allocated outside the capture
+            torch.cuda.synchronize()
+            g = capture(lambda: [fn(i) for i in range(aring)])
+            g.replay()
+            torch.cuda.synchronize()
+            reps = max(1, math.ceil(MIN_LAUNCHES / aring))
+            a_, b_ = ev(), ev()
+            a_.record(stream)
+            for _ in range(reps):
+                g.replay()
+            b_.record(stream)
+            torch.cuda.synchronize()
+            us = a_.elapsed_time(b_) * 1e3 / (reps * aring)
+            del g
+            d = {"us": round(us, 3), "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
+                 "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+            if nflop:
+                d["TFLOP/s"] = round(nflop / (us * 1e-6) / 1e12, 1)
+            return d
+
+        for r in WIDTHS:
+            ab4 = sum(alg_bytes(1, mt["n"], mt["k"], r) for mt in amats)
+            d = {"qkvo_one_launch": apiece(lambda i: mq.linear_mixed(attn_calls(i, r, 1)), ab4)}
+            qkv = apiece(lambda i: mq.linear_mixed(attn_calls(i, r, 1, (0, 1, 2))),
+                         sum(alg_bytes(1, amats[j]["n"], amats[j]["k"], r) for j in (0, 1, 2)))
+            o = apiece(lambda i: mq.linear_mixed(attn_calls(i, r, 1, (3,))), alg_bytes(1, 4096, 4096, r))
+            d["dependent_block_us"] = round(qkv["us"] + o["us"], 3)
+            if r in (2, 4, 8):
+                for m in (16, 64):
+                    # the four skinny calls one after another (each a launch of its own)
+                    byt = sum(alg_bytes(m, mt["n"], mt["k"], r) for mt in amats)
+                    fl = 2.0 * m * sum(mt["n"] * mt["k"] for mt in amats)
+                    d[f"m{m}_four_calls"] = apiece(lambda i: mq.linear_mixed(attn_calls(i, r, m)), byt, fl)
+            attn[str(r)] = d
+            log(f"[bench] attention r={r}: one launch {d['qkvo_one_launch']['us']} us "
+                f"({d['qkvo_one_launch']['frac_hbm'] * 100:.1f}% HBM), dependent block {d['dependent_block_us']} us")
+        del amats
+
     # ---------------- prefill (M = 2048, bf16) ----------------
     prefill = None
     if not args.no_prefill:
@@ -467,6 +542,7 @@ def main():
         "frac_hbm_step": round(value / HBM_PEAK_GBS, 4),
         "prefill": prefill,
         "per_r": per_r,
+        "attention": attn,
         "eager": eager,
         "skinny": skinny,
         "mixnmatch": mix,

@@ -29,6 +29,8 @@ C_BITS = 8
 # Workload shapes.  Llama-3.1-8B FFN: hidden 4096, FFN 14336.  Gemma-2-9B FFN:
 # hidden 3584, FFN 14336.
 LLAMA8B_FFN = (("gate", 14336, 4096), ("up", 14336, 4096), ("down", 4096, 14336))
+# Llama-3.1-8B attention projections (32 query heads, 8 key/value heads of 128)
+LLAMA8B_ATTN = (("q", 4096, 4096), ("k", 1024, 4096), ("v", 1024, 4096), ("o", 4096, 4096))
 GEMMA9B_FFN = (("gate", 14336, 3584), ("up", 14336, 3584), ("down", 3584, 14336))
 GEMMA9B_BLOCKS = 42
 

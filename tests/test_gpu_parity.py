@@ -438,6 +438,36 @@ def test_llama_ffn_prefill_2048(mq, llama_ffn, r):
         check_y(y, lay, x, r, O.PREFIX, w64=w64_of(tid, lay, r, O.PREFIX))
 
 
+@pytest.fixture(scope="module")
+def llama_attn(mq):
+    out = []
+    for tid, (name, n, k) in enumerate(synth.LLAMA8B_ATTN):
+        lay = synth.make_layer(cfg_id=12, tensor_id=tid, n=n, k=k, m=0, group=128, outlier_frac=1e-3)
+        q, s, z = to_dev(lay)
+        out.append((10 + tid, lay, mq.pack_parent(q), s, z))
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("r", WIDTHS)
+def test_llama_attention_projections(mq, llama_attn, r):
+    # q/o 4096 -> 4096 and k/v 4096 -> 1024: decode (the four calls in one
+    # launch through mq_linear_mixed, and alone) and skinny batches, every output
+    for tid, lay, pk, s, z in llama_attn:
+        w64 = w64_of(tid, lay, r, O.PREFIX)
+        for m in (1, 16, 64) if r in (2, 4, 8) else (1,):
+            x = synth.activations(synth.rng_for(12, 50 + m, r), m, lay.k, "f16")
+            y = mq.linear(x.to(DEV), pk.truncated(r), r, O.PREFIX, 128, s, z)
+            check_y(y, lay, x, r, O.PREFIX, w64=w64)
+    xs = [synth.activations(synth.rng_for(12, 90 + i, r), 1, lay.k, "f16") for i, (_, lay, _, _, _) in
+          enumerate(llama_attn)]
+    calls = [mq.Call(x=x.to(DEV), packed=pk.truncated(r), r=r, rule=O.PREFIX, group=128, scales=s, zeros=z)
+             for x, (_, lay, pk, s, z) in zip(xs, llama_attn)]
+    outs = mq.linear_mixed(calls)
+    for c, y in zip(calls, outs):
+        assert torch.equal(y, mq.linear(c.x, c.packed, c.r, c.rule, c.group, c.scales, c.zeros))
+
+
 @pytest.mark.parametrize("m,dt", [(1, "f16"), (256, "bf16")])
 def test_gemma_mixnmatch_blocks(mq, m, dt):
     widths = synth.mixnmatch_widths()
