@@ -477,6 +477,36 @@ def main():
             del ys, calls, ref
         del blocks
 
+    # ---------------- reference: device copies at the decode launch sizes ----------------
+    # torch's device copy over a ring of buffers (> 1 GiB per pass): read and
+    # write bytes over the copy time, the streaming rate one launch of that size
+    # reaches without any arithmetic
+    copy_ref = None
+    if not args.no_pieces:
+        copy_ref = {}
+        for name, nbytes in (("r2_step_launch", bytes_r[2]), ("r8_step_launch", bytes_r[8])):
+            half = (nbytes // 2 + 4095) // 4096 * 4096
+            nbuf = max(4, math.ceil(RING_BYTES / (2 * half)))
+            src = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(nbuf)]
+            dst = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(nbuf)]
+            for i in range(nbuf):
+                dst[i].copy_(src[i])
+            torch.cuda.synchronize()
+            reps = max(nbuf, MIN_LAUNCHES)
+            a_, b_ = ev(), ev()
+            a_.record(stream)
+            for i in range(reps):
+                dst[i % nbuf].copy_(src[i % nbuf])
+            b_.record(stream)
+            torch.cuda.synchronize()
+            us = a_.elapsed_time(b_) * 1e3 / reps
+            copy_ref[name] = {"bytes_moved": 2 * half, "us": round(us, 3),
+                              "GB/s": round(2 * half / (us * 1e-6) / 1e9, 1),
+                              "frac_hbm": round(2 * half / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+            del src, dst
+        log(f"[bench] device copy reference: " + ", ".join(f"{k} {v['us']} us ({v['frac_hbm'] * 100:.1f}%)"
+                                                           for k, v in copy_ref.items()))
+
     if args.copy_calib_mib > 0:
         nb = args.copy_calib_mib << 20
         src = torch.empty(nb, dtype=torch.uint8, device=dev)
@@ -543,6 +573,7 @@ def main():
         "prefill": prefill,
         "per_r": per_r,
         "attention": attn,
+        "copy_reference": copy_ref,
         "eager": eager,
         "skinny": skinny,
         "mixnmatch": mix,

@@ -23,7 +23,15 @@
  *                code = q >> (8-r);  v = code * 2^(8-r) + delta_r,
  *                delta_r = (2^(8-r) - 1) / 2 (centre of the cell).
  *                Reads exactly r bits per weight.
- *   At r = 8 both rules are the identity v = q.
+ *   MQ_ROUND_EXTRA -- Extra-Precision MatQuant ("Matryoshka Quantization |
+ *                Summary", section 7 "Errata": the slice without the clamp):
+ *                code = round(q / 2^(8-r)), ties upward, in 0..2^r (2^r + 1
+ *                levels); v = code * 2^(8-r), up to 256 (unsigned 234 at r = 2
+ *                gives 256).  Reads the same planes as MQ_ROUND.  The pages
+ *                give no storage format for the extra bit (they describe it
+ *                only as sparse, about 2.05 bits per weight at r = 2); here the
+ *                value is rebuilt from the r + 1 bits the planes hold.
+ *   At r = 8 every rule is the identity v = q.
  * Dequantization: w_hat = s * (v - z).  With an fp16 scale and an integer
  * zero point this is exact in fp32.
  *
@@ -35,7 +43,8 @@
  *   plane 3: code bits 3..2   (2 bits/weight)
  *   plane 4: code bits 1..0   (2 bits/weight)
  * A width-r call reads planes 0..P-1 only, P = mq_planes_needed(r, rule):
- * PREFIX r = 2,3,4,6,8 -> P = 1,2,3,4,5; ROUND r = 2,3,4,6 -> P = 2,3,4,5.
+ * PREFIX r = 2,3,4,6,8 -> P = 1,2,3,4,5; ROUND and ROUND_EXTRA r = 2,3,4,6
+ * -> P = 2,3,4,5.
  * Each plane is a row-major [n][k/32] array of 32-code units (8 bytes for a
  * 2-bit plane, 4 bytes for a 1-bit plane).  Inside a unit, the 32 codes'
  * fields are interleaved so that shifting a unit word and masking it yields
@@ -86,12 +95,12 @@ typedef enum {
   MQ_ENOPLANE = 5,   /* a plane that (r, rule) needs is NULL                 */
   MQ_EDTYPE = 6,     /* dtype not allowed for this argument                  */
   MQ_EHIP = 7,       /* a kernel launch failed                               */
-  MQ_ERULE = 8,      /* rule not MQ_PREFIX or MQ_ROUND                       */
+  MQ_ERULE = 8,      /* rule not MQ_PREFIX, MQ_ROUND or MQ_ROUND_EXTRA       */
   MQ_ESIZE = 9       /* a size exceeds what the kernels index (see below)    */
 } mq_status;
 
 typedef enum { MQ_F32 = 0, MQ_F16 = 1, MQ_BF16 = 2 } mq_dtype;
-typedef enum { MQ_PREFIX = 0, MQ_ROUND = 1 } mq_rule;
+typedef enum { MQ_PREFIX = 0, MQ_ROUND = 1, MQ_ROUND_EXTRA = 2 } mq_rule;
 
 #define MQ_NPLANES 5
 
@@ -149,8 +158,8 @@ size_t mq_linear_workspace_bytes(int32_t m, int32_t n, int32_t k);
  * Kernel choice: fp16 x with m <= 4 and bf16 x with m == 1 (k <= 16384)
  * stream the planes with a register GEMV; other m in 2..64 with k % 256 == 0
  * take the skinny MFMA path (weights dequantized straight into MFMA operand
- * registers); everything else runs the MFMA GEMM that dequantizes weight
- * tiles into LDS. */
+ * registers; not for MQ_ROUND_EXTRA); everything else runs the MFMA GEMM
+ * that dequantizes weight tiles into LDS. */
 mq_status mq_linear(const void* x, int32_t x_dtype, int32_t m, const mq_packed* w, int32_t r,
                     int32_t rule, int32_t group, const uint16_t* scales, const uint16_t* zeros,
                     void* y, void* workspace, size_t workspace_bytes, void* stream);
@@ -194,7 +203,8 @@ mq_status mq_linear_mixed(const mq_call* calls, int32_t n_calls, void* workspace
                           size_t workspace_bytes, int32_t* failed_call, void* stream);
 
 /* Test support (same device functions as the GEMMs).
- * mq_slice_codes: codes_out [n, k] uint8 = the r-bit code (0..2^r - 1).
+ * mq_slice_codes: codes_out [n, k] uint8 = the r-bit code (0..2^r - 1; 0..2^r
+ * for MQ_ROUND_EXTRA).
  * mq_dequant: w_out [n, k] of dtype out_dtype (F32 exact; F16/BF16 one
  * round-to-nearest-even from the exact value). */
 mq_status mq_slice_codes(const mq_packed* w, int32_t r, int32_t rule, uint8_t* codes_out,

@@ -12,7 +12,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmq.so")
 
 MQ_F32, MQ_F16, MQ_BF16 = 0, 1, 2
-MQ_PREFIX, MQ_ROUND = 0, 1
+MQ_PREFIX, MQ_ROUND, MQ_ROUND_EXTRA = 0, 1, 2
 NPLANES = 5
 
 STATUS = {

@@ -16,6 +16,11 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool valid_width(int r) { return r == 2 || r == 3 || r == 4 || r == 6 || r == 8; }
 
+bool valid_rule(int rule) { return rule == MQ_PREFIX || rule == MQ_ROUND || rule == MQ_ROUND_EXTRA; }
+
+// the kernels' rule constants are the mq_rule values
+static_assert(MQ_PREFIX == kRulePrefix && MQ_ROUND == kRuleRound && MQ_ROUND_EXTRA == kRuleExtra, "rule values");
+
 mq_status check_shape(int n, int k) {
   if (n <= 0 || k <= 0) return MQ_EINVAL;
   if (k % 64) return MQ_ESHAPE;
@@ -33,9 +38,9 @@ mq_status check_packed(const mq_packed* w, int r, int rule, PlanePtrs* out) {
   if (!w) return MQ_EINVAL;
   mq_status st = check_shape(w->n, w->k);
   if (st != MQ_OK) return st;
-  if (rule != MQ_PREFIX && rule != MQ_ROUND) return MQ_ERULE;
+  if (!valid_rule(rule)) return MQ_ERULE;
   if (!valid_width(r)) return MQ_EWIDTH;
-  const int np = planes_needed(r, rule == MQ_ROUND);
+  const int np = planes_needed(r, rule);
   for (int p = 0; p < MQ_NPLANES; ++p) {
     out->p[p] = static_cast<const uint32_t*>(w->plane[p]);
     if (p < np) {
@@ -86,12 +91,12 @@ mq_status run_linear(const void* x, int x_dtype, int m, const mq_packed* w, int 
   a.k = w->k;
   a.group = group;
   a.r = r;
-  a.round_rule = rule == MQ_ROUND;
+  a.rule = rule;
   a.bf16 = x_dtype == MQ_BF16;
   hipError_t e;
   if (gemv_eligible(m, w->k, a.bf16)) {
     e = launch_gemv_multi(&a, 1, s);
-  } else if (skinny_eligible(m, w->k)) {
+  } else if (skinny_eligible(m, w->k, rule)) {
     const bool ws_ok = workspace && aligned16(workspace);
     e = launch_skinny(a, ws_ok ? workspace : nullptr, ws_ok ? workspace_bytes : 0, s);
   } else {
@@ -117,7 +122,7 @@ bool writes_into(const mq_call& c, const mq_call& d) {
   if (overlaps(c.y, yc, d.x, x_bytes(d)) || overlaps(c.y, yc, d.y, y_bytes(d))) return true;
   const size_t sz = (size_t)d.w->n * (size_t)(d.w->k / d.group) * 2;
   if (overlaps(c.y, yc, d.scales, sz) || overlaps(c.y, yc, d.zeros, sz)) return true;
-  const int np = planes_needed(d.r, d.rule == MQ_ROUND);
+  const int np = planes_needed(d.r, d.rule);
   for (int p = 0; p < np; ++p)
     if (overlaps(c.y, yc, d.w->plane[p], (size_t)d.w->n * (size_t)d.w->k * kPlaneBits[p] / 8)) return true;
   return false;
@@ -146,7 +151,7 @@ LinearArgs call_args(const mq_call& c, const PlanePtrs& pl) {
   a.k = c.w->k;
   a.group = c.group;
   a.r = c.r;
-  a.round_rule = c.rule == MQ_ROUND;
+  a.rule = c.rule;
   a.bf16 = c.x_dtype == MQ_BF16;
   return a;
 }
@@ -201,7 +206,7 @@ const char* mq_status_str(mq_status s) {
     case MQ_ENOPLANE: return "MQ_ENOPLANE: a plane needed by (width, rule) is NULL";
     case MQ_EDTYPE: return "MQ_EDTYPE: unsupported dtype";
     case MQ_EHIP: return "MQ_EHIP: kernel launch failed";
-    case MQ_ERULE: return "MQ_ERULE: rule must be MQ_PREFIX or MQ_ROUND";
+    case MQ_ERULE: return "MQ_ERULE: rule must be MQ_PREFIX, MQ_ROUND or MQ_ROUND_EXTRA";
     case MQ_ESIZE: return "MQ_ESIZE: size out of range";
   }
   return "MQ_UNKNOWN";
@@ -213,8 +218,8 @@ size_t mq_plane_bytes(int32_t n, int32_t k, int32_t plane) {
 }
 
 int32_t mq_planes_needed(int32_t r, int32_t rule) {
-  if (!valid_width(r) || (rule != MQ_PREFIX && rule != MQ_ROUND)) return -1;
-  return planes_needed(r, rule == MQ_ROUND);
+  if (!valid_width(r) || !valid_rule(rule)) return -1;
+  return planes_needed(r, rule);
 }
 
 mq_status mq_pack_parent(const uint8_t* codes, int32_t n, int32_t k, const mq_packed* out, void* stream) {
@@ -237,7 +242,11 @@ size_t mq_linear_workspace_bytes(int32_t m, int32_t n, int32_t k) {
   if (m <= kGemvMaxM && k <= kGemvMaxK && m == 1) return 0;
   // the dtype is not known here: fp16 batches of up to 4 rows take the GEMV
   // (no workspace), bf16 ones the skinny path, so size for the latter
-  if (skinny_eligible(m, k)) return skinny_workspace_bytes(m, n, k);
+  // the unclamped rule takes the GEMM at these m as well: size for either
+  if (skinny_shape(m, k)) {
+    const size_t a = skinny_workspace_bytes(m, n, k), b = gemm_workspace_bytes(m, n, k);
+    return a > b ? a : b;
+  }
   return gemm_workspace_bytes(m, n, k);
 }
 
@@ -330,7 +339,7 @@ mq_status mq_slice_codes(const mq_packed* w, int32_t r, int32_t rule, uint8_t* c
   if (st != MQ_OK) return st;
   if (!codes_out) return MQ_EINVAL;
   if (!aligned16(codes_out)) return MQ_EALIGN;
-  return launch_slice(pl, w->n, w->k, r, rule == MQ_ROUND, codes_out, static_cast<hipStream_t>(stream)) == hipSuccess
+  return launch_slice(pl, w->n, w->k, r, rule, codes_out, static_cast<hipStream_t>(stream)) == hipSuccess
              ? MQ_OK
              : MQ_EHIP;
 }
@@ -345,7 +354,7 @@ mq_status mq_dequant(const mq_packed* w, int32_t r, int32_t rule, int32_t group,
   if (out_dtype != MQ_F32 && out_dtype != MQ_F16 && out_dtype != MQ_BF16) return MQ_EDTYPE;
   if (!w_out) return MQ_EINVAL;
   if (!aligned16(w_out)) return MQ_EALIGN;
-  return launch_dequant(pl, w->n, w->k, r, rule == MQ_ROUND, group, scales, zeros, out_dtype, w_out,
+  return launch_dequant(pl, w->n, w->k, r, rule, group, scales, zeros, out_dtype, w_out,
                         static_cast<hipStream_t>(stream)) == hipSuccess
              ? MQ_OK
              : MQ_EHIP;

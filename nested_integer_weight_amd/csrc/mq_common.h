@@ -38,9 +38,18 @@ __host__ __device__ constexpr int planes_for_bits(int bits) {
 __host__ __device__ constexpr int bits_of_planes(int P) {
   return P <= 0 ? 0 : P == 1 ? 2 : P == 2 ? 3 : P == 3 ? 4 : P == 4 ? 6 : 8;
 }
-// planes read by a width-r call: PREFIX reads r bits, ROUND reads r+1 (r < 8)
-__host__ __device__ constexpr int planes_needed(int r, int round_rule) {
-  return planes_for_bits((round_rule && r < 8) ? r + 1 : r);
+// Slicing rules, the RULE template parameter of every kernel (the values of
+// mq_rule in mq.h):
+//   kRulePrefix MatGPTQ true prefix: the r most significant bits, + delta_r
+//   kRuleRound  MatQuant: round half up on the (r+1)-th bit, clamp to 2^r - 1
+//   kRuleExtra  Extra-Precision MatQuant: the same rounding without the clamp,
+//               2^r + 1 levels, values up to 256
+constexpr int kRulePrefix = 0, kRuleRound = 1, kRuleExtra = 2;
+
+// planes read by a width-r call: the true prefix reads r bits, both rounded
+// rules r + 1 (r < 8), each rounded up to a plane boundary
+__host__ __device__ constexpr int planes_needed(int r, int rule) {
+  return planes_for_bits((rule && r < 8) ? r + 1 : r);
 }
 __host__ __device__ constexpr uint32_t rep4(uint32_t b) { return b * 0x01010101u; }
 
@@ -88,18 +97,19 @@ __device__ __forceinline__ uint32_t assemble_word(const uint32_t* unit) {
   return assemble_word_impl<NP, J, 1>(unit, plane_shifted<0, J>(unit) & plane_mask<0>());
 }
 
-// Byte-domain value of the r-bit slice for four codes packed in one word,
-// before any centring offset:
-//   PREFIX: v = (q >> (8-r)) << (8-r)                       (<= 255, exact in a byte)
-//   ROUND : v = min(round_half_up(q / 2^(8-r)), 2^r - 1) << (8-r)
-// ROUND can overflow a byte before the clamp, so it is evaluated in 16-bit
-// lanes: `lo`/`hi` receive codes {0,1} and {2,3} as u16 pairs.
-template <int R, int ROUND>
+// Value of the r-bit slice in the 8-bit code space for four codes packed in
+// one word (bytes as assembled from the planes), before any centring offset:
+//   kRulePrefix: v = (q >> (8-r)) << (8-r)                        (<= 255)
+//   kRuleRound:  v = min(round_half_up(q / 2^(8-r)), 2^r - 1) << (8-r)
+//   kRuleExtra:  v = round_half_up(q / 2^(8-r)) << (8-r)           (<= 256)
+// The rounding can overflow a byte, so it is evaluated in 16-bit lanes:
+// `lo`/`hi` receive codes {0,1} and {2,3} as u16 pairs.
+template <int R, int RULE>
 __device__ __forceinline__ void slice_pairs(uint32_t bytes, uint32_t& lo, uint32_t& hi) {
   // v_perm_b32 selector: byte 0x0c yields 0x00
   lo = __builtin_amdgcn_perm(0u, bytes, 0x0c010c00u);
   hi = __builtin_amdgcn_perm(0u, bytes, 0x0c030c02u);
-  if constexpr (ROUND && R < 8) {
+  if constexpr (RULE && R < 8) {
     constexpr uint32_t keep = (0xFFu << (7 - R)) & 0xFFu;  // top r+1 bits
     constexpr uint32_t half = 1u << (7 - R);               // the (r+1)-th bit
     constexpr uint32_t lim = 256u - (1u << (8 - R));       // (2^r - 1) << (8-r)
@@ -107,25 +117,47 @@ __device__ __forceinline__ void slice_pairs(uint32_t bytes, uint32_t& lo, uint32
     u16x2 a = __builtin_bit_cast(u16x2, lo & (keep * 0x10001u));
     u16x2 b = __builtin_bit_cast(u16x2, hi & (keep * 0x10001u));
     const u16x2 hv = {(unsigned short)half, (unsigned short)half};
-    const u16x2 lv = {(unsigned short)lim, (unsigned short)lim};
     a = a + (a & hv);
     b = b + (b & hv);
-    a = __builtin_elementwise_min(a, lv);
-    b = __builtin_elementwise_min(b, lv);
+    if constexpr (RULE == kRuleRound) {
+      const u16x2 lv = {(unsigned short)lim, (unsigned short)lim};
+      a = __builtin_elementwise_min(a, lv);
+      b = __builtin_elementwise_min(b, lv);
+    }
     lo = __builtin_bit_cast(uint32_t, a);
     hi = __builtin_bit_cast(uint32_t, b);
   }
 }
 
-// Same slice, kept as four bytes (valid after the clamp: v <= 255).
-template <int R, int ROUND>
+// Same slice, kept as four bytes (v <= 255: not for the unclamped rule).
+template <int R, int RULE>
 __device__ __forceinline__ uint32_t slice_bytes(uint32_t bytes) {
-  if constexpr (ROUND && R < 8) {
+  static_assert(RULE != kRuleExtra || R == 8, "the unclamped slice reaches 256: use slice_pairs");
+  if constexpr (RULE && R < 8) {
     uint32_t lo, hi;
-    slice_pairs<R, ROUND>(bytes, lo, hi);
+    slice_pairs<R, RULE>(bytes, lo, hi);
     return __builtin_amdgcn_perm(hi, lo, 0x06040200u);
   } else {
     return bytes;
+  }
+}
+
+// The four slice values of a word as floats, for every rule.
+template <int R, int RULE>
+__device__ __forceinline__ void slice_f32x4(uint32_t bytes, float* f) {
+  if constexpr (RULE == kRuleExtra && R < 8) {
+    uint32_t lo, hi;
+    slice_pairs<R, RULE>(bytes, lo, hi);
+    f[0] = (float)(lo & 0xFFFFu);
+    f[1] = (float)(lo >> 16);
+    f[2] = (float)(hi & 0xFFFFu);
+    f[3] = (float)(hi >> 16);
+  } else {
+    const uint32_t v = slice_bytes<R, RULE>(bytes);
+    f[0] = (float)(v & 0xFFu);
+    f[1] = (float)((v >> 8) & 0xFFu);
+    f[2] = (float)((v >> 16) & 0xFFu);
+    f[3] = (float)(v >> 24);
   }
 }
 

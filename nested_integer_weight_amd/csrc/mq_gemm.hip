@@ -69,16 +69,16 @@ __device__ __forceinline__ floatx4 mfma16x16x32(const uint4& a, const uint4& b, 
 // Per-thread state of one workgroup tile.  Helpers are force-inlined member
 // functions (not lambdas capturing arrays by reference), so the staging
 // arrays are scalarised into registers instead of living in memory.
-template <int R, int ROUND, int BF16, int BM, int BN, int WM, int WN>
+template <int R, int RULE, int BF16, int BM, int BN, int WM, int WN>
 struct GemmTile {
   static constexpr int T = 64 * WM * WN;
-  static constexpr int NP = planes_needed(R, ROUND);
+  static constexpr int NP = planes_needed(R, RULE);
   static constexpr int FM = BM / WM / 16;
   static constexpr int FN = BN / WN / 16;
   static constexpr int CX = (BM * 8 + T - 1) / T;  // 16-byte X chunks per thread per step
   static constexpr int CW = BN * 2 / T;             // (row, unit) weight items per thread per step
   static_assert(CW >= 1 && CW * T == BN * 2, "W tile split");
-  static constexpr float kDelta = ROUND ? 0.0f : prefix_delta(R);
+  static constexpr float kDelta = RULE ? 0.0f : prefix_delta(R);
 
   const GemmArgs& a;
   int tid, m0, n0, gpr;
@@ -179,11 +179,12 @@ struct GemmTile {
       uint32_t h[16];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const uint32_t v = slice_bytes<R, ROUND>(bytes[j]);
-        const float w0 = fmaf((float)(v & 0xFFu), s, cz);
-        const float w1 = fmaf((float)((v >> 8) & 0xFFu), s, cz);
-        const float w2 = fmaf((float)((v >> 16) & 0xFFu), s, cz);
-        const float w3 = fmaf((float)(v >> 24), s, cz);
+        float v[4];
+        slice_f32x4<R, RULE>(bytes[j], v);
+        const float w0 = fmaf(v[0], s, cz);
+        const float w1 = fmaf(v[1], s, cz);
+        const float w2 = fmaf(v[2], s, cz);
+        const float w3 = fmaf(v[3], s, cz);
         h[2 * j] = BF16 ? pack_bf16x2(w0, w1) : pack_f16x2(w0, w1);
         h[2 * j + 1] = BF16 ? pack_bf16x2(w2, w3) : pack_f16x2(w2, w3);
       }
@@ -213,9 +214,9 @@ struct GemmTile {
   }
 };
 
-template <int R, int ROUND, int BF16, int BM, int BN, int WM, int WN>
+template <int R, int RULE, int BF16, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs a) {
-  using Tile = GemmTile<R, ROUND, BF16, BM, BN, WM, WN>;
+  using Tile = GemmTile<R, RULE, BF16, BM, BN, WM, WN>;
   constexpr int FM = Tile::FM, FN = Tile::FN;
   // double-buffered LDS tiles: X swizzled row-major, weights fragment-major
   __shared__ uint4 As[2][BM * 8];
@@ -415,29 +416,29 @@ GemmPlan plan_gemm(int m, int n, int k, size_t workspace_bytes) {
   return p;
 }
 
-template <int R, int ROUND, int BF16, int BM, int BN, int WM, int WN>
+template <int R, int RULE, int BF16, int BM, int BN, int WM, int WN>
 static hipError_t gemm_launch_cfg(const GemmArgs& ga, int splits, hipStream_t s) {
   dim3 grid((unsigned)(ga.tiles_m * ga.tiles_n), (unsigned)splits);
-  hipLaunchKernelGGL((gemm_kernel<R, ROUND, BF16, BM, BN, WM, WN>), grid, dim3(64 * WM * WN), 0, s, ga);
+  hipLaunchKernelGGL((gemm_kernel<R, RULE, BF16, BM, BN, WM, WN>), grid, dim3(64 * WM * WN), 0, s, ga);
   return hipGetLastError();
 }
 
-template <int R, int ROUND, int BF16>
+template <int R, int RULE, int BF16>
 static hipError_t gemm_launch_t(const GemmArgs& ga, int cfg, int splits, hipStream_t s) {
   switch (cfg) {
-    case 0: return gemm_launch_cfg<R, ROUND, BF16, 256, 256, 2, 4>(ga, splits, s);
-    case 1: return gemm_launch_cfg<R, ROUND, BF16, 128, 256, 2, 4>(ga, splits, s);
-    case 2: return gemm_launch_cfg<R, ROUND, BF16, 64, 256, 1, 4>(ga, splits, s);
-    case 3: return gemm_launch_cfg<R, ROUND, BF16, 32, 256, 1, 4>(ga, splits, s);
-    case 4: return gemm_launch_cfg<R, ROUND, BF16, 16, 256, 1, 4>(ga, splits, s);
-    case 5: return gemm_launch_cfg<R, ROUND, BF16, 128, 128, 2, 2>(ga, splits, s);
-    default: return gemm_launch_cfg<R, ROUND, BF16, 256, 128, 2, 2>(ga, splits, s);
+    case 0: return gemm_launch_cfg<R, RULE, BF16, 256, 256, 2, 4>(ga, splits, s);
+    case 1: return gemm_launch_cfg<R, RULE, BF16, 128, 256, 2, 4>(ga, splits, s);
+    case 2: return gemm_launch_cfg<R, RULE, BF16, 64, 256, 1, 4>(ga, splits, s);
+    case 3: return gemm_launch_cfg<R, RULE, BF16, 32, 256, 1, 4>(ga, splits, s);
+    case 4: return gemm_launch_cfg<R, RULE, BF16, 16, 256, 1, 4>(ga, splits, s);
+    case 5: return gemm_launch_cfg<R, RULE, BF16, 128, 128, 2, 2>(ga, splits, s);
+    default: return gemm_launch_cfg<R, RULE, BF16, 256, 128, 2, 2>(ga, splits, s);
   }
 }
 
-template <int R, int ROUND>
+template <int R, int RULE>
 static hipError_t gemm_launch_d(const GemmArgs& ga, int bf16, int cfg, int splits, hipStream_t s) {
-  return bf16 ? gemm_launch_t<R, ROUND, 1>(ga, cfg, splits, s) : gemm_launch_t<R, ROUND, 0>(ga, cfg, splits, s);
+  return bf16 ? gemm_launch_t<R, RULE, 1>(ga, cfg, splits, s) : gemm_launch_t<R, RULE, 0>(ga, cfg, splits, s);
 }
 
 hipError_t launch_gemm(const LinearArgs& la, const GemmPlan& plan, void* workspace, hipStream_t s) {
@@ -458,10 +459,11 @@ hipError_t launch_gemm(const LinearArgs& la, const GemmPlan& plan, void* workspa
   ga.to_workspace = splits > 1;
   ga.y = splits > 1 ? workspace : la.y;
   hipError_t e;
-#define MQ_GEMM_CASE(RR)                                                                   \
-  case RR:                                                                                 \
-    e = la.round_rule ? gemm_launch_d<RR, 1>(ga, la.bf16, plan.cfg, splits, s)             \
-                      : gemm_launch_d<RR, 0>(ga, la.bf16, plan.cfg, splits, s);            \
+#define MQ_GEMM_CASE(RR)                                                                            \
+  case RR:                                                                                          \
+    e = la.rule == kRuleExtra ? gemm_launch_d<RR, kRuleExtra>(ga, la.bf16, plan.cfg, splits, s)   \
+        : la.rule == kRuleRound ? gemm_launch_d<RR, kRuleRound>(ga, la.bf16, plan.cfg, splits, s)        \
+                               : gemm_launch_d<RR, kRulePrefix>(ga, la.bf16, plan.cfg, splits, s);      \
     break;
   switch (la.r) {
     MQ_GEMM_CASE(2)

@@ -141,10 +141,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base) 
 // cache-policy operand of the buffer loads: nontemporal (streamed once)
 constexpr int kNontemporal = 2;
 
-template <int R, int ROUND, int MT, int BF16, int ROWS>
+template <int R, int RULE, int MT, int BF16, int ROWS>
 struct GemvWave {
-  static constexpr int NP = planes_needed(R, ROUND);
-  static constexpr bool FAST2 = (R == 2 && !ROUND && !BF16);
+  static constexpr int NP = planes_needed(R, RULE);
+  static constexpr bool FAST2 = (R == 2 && !RULE && !BF16);
   static constexpr int V = ROWS * MT;
   // Rows are loaded and computed in batches of RB rows (two for widths of up
   // to three planes, one for wider ones), PD batches in flight.  Measured on
@@ -154,7 +154,7 @@ struct GemvWave {
   static constexpr int RB = NP <= 3 ? 2 : 1;
   static constexpr int NB = ROWS / RB;
   static constexpr int PD = NP == 4 ? 3 : 2;
-  static constexpr float kDelta = ROUND ? 0.0f : prefix_delta(R);
+  static constexpr float kDelta = RULE ? 0.0f : prefix_delta(R);
   static_assert((V & (V - 1)) == 0 && V <= 32, "values per lane must be a power of two");
   static_assert(NB * RB == ROWS, "row batches");
 
@@ -322,17 +322,17 @@ struct GemvWave {
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             if constexpr (BF16) {
-              const uint32_t v = slice_bytes<R, ROUND>(bytes[j]);
+              float fv[4];
+              slice_f32x4<R, RULE>(bytes[j], fv);
 #pragma unroll
               for (int bb = 0; bb < 4; ++bb) {
-                const float fv = (float)((v >> (8 * bb)) & 0xFFu);
 #pragma unroll
-                for (int mm = 0; mm < MT; ++mm) dot[mm] = fmaf(fv, xf[mm][32 * u + 4 * j + bb], dot[mm]);
+                for (int mm = 0; mm < MT; ++mm) dot[mm] = fmaf(fv[bb], xf[mm][32 * u + 4 * j + bb], dot[mm]);
               }
             } else {
               uint32_t lo, hi;
-              if constexpr (ROUND && R < 8) {
-                slice_pairs<R, ROUND>(bytes[j], lo, hi);
+              if constexpr (RULE && R < 8) {
+                slice_pairs<R, RULE>(bytes[j], lo, hi);
                 lo |= 0x64006400u;
                 hi |= 0x64006400u;
               } else {
@@ -420,9 +420,9 @@ struct GemvWave {
 // kernel arguments.  A row group of one wave (k <= 4096) shares the
 // activations of its call with the other three waves through LDS; wider rows
 // split the slices over 2 or 4 waves and each lane loads its own.
-template <int R, int ROUND, int MT, int BF16, int ROWS>
+template <int R, int RULE, int MT, int BF16, int ROWS>
 __global__ __launch_bounds__(256) void gemv_multi_kernel(GemvLaunch a) {
-  using Wave = GemvWave<R, ROUND, MT, BF16, ROWS>;
+  using Wave = GemvWave<R, RULE, MT, BF16, ROWS>;
   __shared__ float red[4 * Wave::V];
   __shared__ uint4 xlds[MT * 8 * 64];  // [token][piece][slice] for one-wave rows
   const int it = (int)blockIdx.x;
@@ -482,7 +482,7 @@ __global__ __launch_bounds__(256) void gemv_multi_kernel(GemvLaunch a) {
 
 int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 
-template <int R, int ROUND, int MT, int BF16>
+template <int R, int RULE, int MT, int BF16>
 hipError_t gemv_launch_t(const LinearArgs* la, int ncalls, hipStream_t s) {
   constexpr int ROWS = gemv_rows(MT);
   GemvLaunch a;
@@ -509,34 +509,37 @@ hipError_t gemv_launch_t(const LinearArgs* la, int ncalls, hipStream_t s) {
   for (int i = ncalls; i < kGemvMaxCalls; ++i) a.c[i] = a.c[ncalls - 1];
   a.ncalls = ncalls;
   a.m = la[0].m;
-  hipLaunchKernelGGL((gemv_multi_kernel<R, ROUND, MT, BF16, ROWS>), dim3((unsigned)items), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((gemv_multi_kernel<R, RULE, MT, BF16, ROWS>), dim3((unsigned)items), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-template <int R, int ROUND, int BF16>
+template <int R, int RULE, int BF16>
 hipError_t gemv_launch_m(const LinearArgs* a, int n, hipStream_t s) {
   if constexpr (BF16) {
-    return gemv_launch_t<R, ROUND, 1, 1>(a, n, s);  // bf16: m == 1 only
+    return gemv_launch_t<R, RULE, 1, 1>(a, n, s);  // bf16: m == 1 only
   } else {
     switch (a[0].m) {
-      case 1: return gemv_launch_t<R, ROUND, 1, 0>(a, n, s);
-      case 2: return gemv_launch_t<R, ROUND, 2, 0>(a, n, s);
-      default: return gemv_launch_t<R, ROUND, 4, 0>(a, n, s);
+      case 1: return gemv_launch_t<R, RULE, 1, 0>(a, n, s);
+      case 2: return gemv_launch_t<R, RULE, 2, 0>(a, n, s);
+      default: return gemv_launch_t<R, RULE, 4, 0>(a, n, s);
     }
   }
 }
 
-template <int R, int ROUND>
+template <int R, int RULE>
 hipError_t gemv_launch_d(const LinearArgs* a, int n, hipStream_t s) {
-  return a[0].bf16 ? gemv_launch_m<R, ROUND, 1>(a, n, s) : gemv_launch_m<R, ROUND, 0>(a, n, s);
+  return a[0].bf16 ? gemv_launch_m<R, RULE, 1>(a, n, s) : gemv_launch_m<R, RULE, 0>(a, n, s);
 }
 
 }  // namespace
 
 hipError_t launch_gemv_multi(const LinearArgs* a, int ncalls, hipStream_t s) {
   if (ncalls < 1 || ncalls > kGemvMaxCalls) return hipErrorInvalidValue;
-#define MQ_GEMV_CASE(RR) \
-  case RR: return a[0].round_rule ? gemv_launch_d<RR, 1>(a, ncalls, s) : gemv_launch_d<RR, 0>(a, ncalls, s);
+#define MQ_GEMV_CASE(RR)                                                               \
+  case RR:                                                                             \
+    return a[0].rule == kRuleExtra ? gemv_launch_d<RR, kRuleExtra>(a, ncalls, s)     \
+           : a[0].rule == kRuleRound ? gemv_launch_d<RR, kRuleRound>(a, ncalls, s)          \
+                                    : gemv_launch_d<RR, kRulePrefix>(a, ncalls, s);
   switch (a[0].r) {
     MQ_GEMV_CASE(2)
     MQ_GEMV_CASE(3)

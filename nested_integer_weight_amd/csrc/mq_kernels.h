@@ -12,9 +12,9 @@
 namespace mq {
 
 hipError_t launch_pack(const uint8_t* codes, int n, int k, uint32_t* const planes[5], hipStream_t s);
-hipError_t launch_slice(const PlanePtrs& pl, int n, int k, int r, int round_rule, uint8_t* out,
+hipError_t launch_slice(const PlanePtrs& pl, int n, int k, int r, int rule, uint8_t* out,
                         hipStream_t s);
-hipError_t launch_dequant(const PlanePtrs& pl, int n, int k, int r, int round_rule, int group,
+hipError_t launch_dequant(const PlanePtrs& pl, int n, int k, int r, int rule, int group,
                           const uint16_t* scales, const uint16_t* zeros, int out_dtype, void* out,
                           hipStream_t s);
 
@@ -24,7 +24,8 @@ struct LinearArgs {
   PlanePtrs pl;
   const uint16_t* scales;
   const uint16_t* zeros;
-  int m, n, k, group, r, round_rule;
+  int m, n, k, group, r;
+  int rule;  // kRulePrefix, kRuleRound or kRuleExtra
   int bf16;  // 1: x/y are bf16, 0: fp16
 };
 
@@ -44,7 +45,9 @@ hipError_t launch_gemv_multi(const LinearArgs* a, int ncalls, hipStream_t s);
 // MFMA skinny path (weights dequantized straight into MFMA operand registers,
 // activations shared through LDS): 2 <= m <= 64 with k a multiple of 256.
 constexpr int kSkinnyMaxM = 64;
-__host__ inline bool skinny_eligible(int m, int k) { return m >= 2 && m <= kSkinnyMaxM && k % 256 == 0; }
+// (true prefix and rounded slice; the unclamped rule takes the GEMM)
+__host__ inline bool skinny_shape(int m, int k) { return m >= 2 && m <= kSkinnyMaxM && k % 256 == 0; }
+__host__ inline bool skinny_eligible(int m, int k, int rule) { return skinny_shape(m, k) && rule != kRuleExtra; }
 struct SkinnyPlan {
   int splits;            // k ranges (1 = no workspace)
   int rounds_per_split;  // 256-wide k rounds per range

@@ -8,7 +8,8 @@
 // rebuild four codes as bytes.
 //
 // The export kernels rebuild codes through exactly the same device helpers
-// (assemble_word / slice_bytes) that the GEMV and the GEMM use.
+// (assemble_word, slice_pairs / slice_bytes / slice_f32x4) that the GEMV and
+// the GEMM use.
 #include "mq_common.h"
 #include "mq_kernels.h"
 
@@ -69,9 +70,9 @@ __device__ __forceinline__ void assemble_unit(const uint32_t* rec, uint32_t* out
   }
 }
 
-template <int R, int ROUND>
+template <int R, int RULE>
 __global__ __launch_bounds__(256) void slice_kernel(PlanePtrs pl, size_t n_units, uint8_t* __restrict__ out) {
-  constexpr int NP = planes_needed(R, ROUND);
+  constexpr int NP = planes_needed(R, RULE);
   size_t u = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (u >= n_units) return;
   uint32_t rec[kUnitWords];
@@ -81,9 +82,19 @@ __global__ __launch_bounds__(256) void slice_kernel(PlanePtrs pl, size_t n_units
   uint32_t res[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    uint32_t v = slice_bytes<R, ROUND>(bytes[j]);
-    if constexpr (!ROUND) v &= rep4((0xFFu << (8 - R)) & 0xFFu);  // exactly r bits
-    res[j] = (v >> (8 - R)) & rep4(0xFFu >> (8 - R));                // r-bit code
+    if constexpr (RULE == kRuleExtra && R < 8) {
+      // the unclamped code reaches 2^r: taken from the 16-bit lanes (the low
+      // 8 - r bits of each lane are zero, so the shifts move no bits between lanes)
+      uint32_t lo, hi;
+      slice_pairs<R, RULE>(bytes[j], lo, hi);
+      lo >>= 8 - R;
+      hi >>= 8 - R;
+      res[j] = __builtin_amdgcn_perm(hi, lo, 0x06040200u);  // codes <= 128 fit a byte
+    } else {
+      uint32_t v = slice_bytes<R, RULE>(bytes[j]);
+      if constexpr (!RULE) v &= rep4((0xFFu << (8 - R)) & 0xFFu);  // exactly r bits
+      res[j] = (v >> (8 - R)) & rep4(0xFFu >> (8 - R));                // r-bit code
+    }
   }
   uint4* dst = reinterpret_cast<uint4*>(out + u * 32);
   dst[0] = make_uint4(res[0], res[1], res[2], res[3]);
@@ -91,13 +102,13 @@ __global__ __launch_bounds__(256) void slice_kernel(PlanePtrs pl, size_t n_units
 }
 
 // out_dtype: 0 = f32, 1 = f16, 2 = bf16
-template <int R, int ROUND, int OUT>
+template <int R, int RULE, int OUT>
 __global__ __launch_bounds__(256) void dequant_kernel(PlanePtrs pl, size_t n_units, int units_per_row,
                                                       int groups_per_row, int units_per_group,
                                                       const uint16_t* __restrict__ scales,
                                                       const uint16_t* __restrict__ zeros,
                                                       void* __restrict__ out) {
-  constexpr int NP = planes_needed(R, ROUND);
+  constexpr int NP = planes_needed(R, RULE);
   size_t u = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (u >= n_units) return;
   size_t row = u / (size_t)units_per_row;
@@ -105,7 +116,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(PlanePtrs pl, size_t n_uni
   size_t g = row * (size_t)groups_per_row + (size_t)(col_unit / units_per_group);
   float s = h2f(scales[g]);
   float z = h2f(zeros[g]);
-  float c = ((ROUND ? 0.0f : prefix_delta(R)) - z) * s;  // exact: half-integer * fp16
+  float c = ((RULE ? 0.0f : prefix_delta(R)) - z) * s;  // exact: half-integer * fp16
   uint32_t rec[kUnitWords];
   load_unit<NP>(pl, u, rec);
   uint32_t bytes[8];
@@ -113,9 +124,10 @@ __global__ __launch_bounds__(256) void dequant_kernel(PlanePtrs pl, size_t n_uni
   float w[32];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    uint32_t v = slice_bytes<R, ROUND>(bytes[j]);
+    float v[4];
+    slice_f32x4<R, RULE>(bytes[j], v);
 #pragma unroll
-    for (int b = 0; b < 4; ++b) w[4 * j + b] = fmaf((float)((v >> (8 * b)) & 0xFFu), s, c);
+    for (int b = 0; b < 4; ++b) w[4 * j + b] = fmaf(v[b], s, c);
   }
   if constexpr (OUT == 0) {
     float4* dst = reinterpret_cast<float4*>(static_cast<float*>(out) + u * 32);
@@ -144,18 +156,19 @@ hipError_t launch_pack(const uint8_t* codes, int n, int k, uint32_t* const plane
   return hipGetLastError();
 }
 
-template <int R, int ROUND>
+template <int R, int RULE>
 static void slice_dispatch_r(const PlanePtrs& pl, size_t n_units, uint8_t* out, hipStream_t s) {
-  hipLaunchKernelGGL((slice_kernel<R, ROUND>), dim3(blocks_for(n_units, 256)), dim3(256), 0, s, pl, n_units,
+  hipLaunchKernelGGL((slice_kernel<R, RULE>), dim3(blocks_for(n_units, 256)), dim3(256), 0, s, pl, n_units,
                      out);
 }
 
-hipError_t launch_slice(const PlanePtrs& pl, int n, int k, int r, int round_rule, uint8_t* out, hipStream_t s) {
+hipError_t launch_slice(const PlanePtrs& pl, int n, int k, int r, int rule, uint8_t* out, hipStream_t s) {
   size_t n_units = (size_t)n * (size_t)(k / 32);
 #define MQ_SLICE_CASE(RR)                                                   \
   case RR:                                                                  \
-    if (round_rule) slice_dispatch_r<RR, 1>(pl, n_units, out, s);           \
-    else slice_dispatch_r<RR, 0>(pl, n_units, out, s);                      \
+    if (rule == kRuleExtra) slice_dispatch_r<RR, kRuleExtra>(pl, n_units, out, s); \
+    else if (rule == kRuleRound) slice_dispatch_r<RR, kRuleRound>(pl, n_units, out, s);     \
+    else slice_dispatch_r<RR, kRulePrefix>(pl, n_units, out, s);                        \
     break;
   switch (r) {
     MQ_SLICE_CASE(2)
@@ -169,27 +182,31 @@ hipError_t launch_slice(const PlanePtrs& pl, int n, int k, int r, int round_rule
   return hipGetLastError();
 }
 
-template <int R, int ROUND>
+template <int R, int RULE>
 static void dequant_dispatch_r(const PlanePtrs& pl, int n, int k, int group, const uint16_t* sc,
                                const uint16_t* zr, int out_dtype, void* out, hipStream_t s) {
   size_t n_units = (size_t)n * (size_t)(k / 32);
   dim3 grid(blocks_for(n_units, 256)), block(256);
   int upr = k / 32, gpr = k / group, upg = group / 32;
   if (out_dtype == 0)
-    hipLaunchKernelGGL((dequant_kernel<R, ROUND, 0>), grid, block, 0, s, pl, n_units, upr, gpr, upg, sc, zr, out);
+    hipLaunchKernelGGL((dequant_kernel<R, RULE, 0>), grid, block, 0, s, pl, n_units, upr, gpr, upg, sc, zr, out);
   else if (out_dtype == 1)
-    hipLaunchKernelGGL((dequant_kernel<R, ROUND, 1>), grid, block, 0, s, pl, n_units, upr, gpr, upg, sc, zr, out);
+    hipLaunchKernelGGL((dequant_kernel<R, RULE, 1>), grid, block, 0, s, pl, n_units, upr, gpr, upg, sc, zr, out);
   else
-    hipLaunchKernelGGL((dequant_kernel<R, ROUND, 2>), grid, block, 0, s, pl, n_units, upr, gpr, upg, sc, zr, out);
+    hipLaunchKernelGGL((dequant_kernel<R, RULE, 2>), grid, block, 0, s, pl, n_units, upr, gpr, upg, sc, zr, out);
 }
 
-hipError_t launch_dequant(const PlanePtrs& pl, int n, int k, int r, int round_rule, int group,
+hipError_t launch_dequant(const PlanePtrs& pl, int n, int k, int r, int rule, int group,
                           const uint16_t* scales, const uint16_t* zeros, int out_dtype, void* out,
                           hipStream_t s) {
 #define MQ_DQ_CASE(RR)                                                                              \
   case RR:                                                                                          \
-    if (round_rule) dequant_dispatch_r<RR, 1>(pl, n, k, group, scales, zeros, out_dtype, out, s);   \
-    else dequant_dispatch_r<RR, 0>(pl, n, k, group, scales, zeros, out_dtype, out, s);              \
+    if (rule == kRuleExtra)                                                                        \
+      dequant_dispatch_r<RR, kRuleExtra>(pl, n, k, group, scales, zeros, out_dtype, out, s);       \
+    else if (rule == kRuleRound)                                                                        \
+      dequant_dispatch_r<RR, kRuleRound>(pl, n, k, group, scales, zeros, out_dtype, out, s);            \
+    else                                                                                            \
+      dequant_dispatch_r<RR, kRulePrefix>(pl, n, k, group, scales, zeros, out_dtype, out, s);           \
     break;
   switch (r) {
     MQ_DQ_CASE(2)

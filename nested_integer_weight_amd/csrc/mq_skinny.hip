@@ -100,10 +100,10 @@ __device__ __forceinline__ uint32_t dq_f16x2(uint32_t magic_pair, f16x2 c, f16x2
 // XB = X buffers per team: 2 (the next round's X is staged while the current
 // one is read) or 1 (staged after a barrier that follows the reads, when two
 // buffers of long rounds would not fit in LDS)
-template <int R, int ROUND, int BF16, int MT, int NT, int RUN, int XB>
+template <int R, int RULE, int BF16, int MT, int NT, int RUN, int XB>
 struct SkinnyWave {
-  static constexpr int NP = planes_needed(R, ROUND);
-  static constexpr float kDelta = ROUND ? 0.0f : prefix_delta(R);
+  static constexpr int NP = planes_needed(R, RULE);
+  static constexpr float kDelta = RULE ? 0.0f : prefix_delta(R);
   static constexpr int KR = kRound * RUN;     // codes per round
   static constexpr int KS = 8 * RUN;          // MFMA k-steps per round
   static constexpr int CPR = KR / 8;          // 16-byte X chunks per activation row and round
@@ -217,8 +217,8 @@ struct SkinnyWave {
   __device__ __forceinline__ u32x4 w_frag() const {
     const uint32_t* u = rec[SLOT][T][I >> 2];
     constexpr int J0 = 2 * (I & 3);
-    const uint32_t w0 = slice_bytes<R, ROUND>(assemble_word<NP, J0>(u));
-    const uint32_t w1 = slice_bytes<R, ROUND>(assemble_word<NP, J0 + 1>(u));
+    const uint32_t w0 = slice_bytes<R, RULE>(assemble_word<NP, J0>(u));
+    const uint32_t w1 = slice_bytes<R, RULE>(assemble_word<NP, J0 + 1>(u));
     if constexpr (BF16) {
       const float s = h2f((uint16_t)sraw[SLOT][T]);
       const float cz = (kDelta - h2f((uint16_t)zraw[SLOT][T])) * s;  // exact
@@ -334,7 +334,7 @@ constexpr int x_buffers() { return (KH == 2 && RUN == 2 && MT >= 3) ? 1 : 2; }
 // weight bytes are in flight per CU.
 // Two waves per SIMD is enough to cover the latency with the prefetch above;
 // asking for more would make the compiler spill the staging registers.
-template <int R, int ROUND, int BF16, int MT, int NT, int KH, int RUN>
+template <int R, int RULE, int BF16, int MT, int NT, int KH, int RUN>
 __global__ __launch_bounds__(256 * KH) __attribute__((amdgpu_waves_per_eu(2, 2))) void skinny_kernel(SkinnyArgs a) {
   constexpr int KR = kRound * RUN;
   constexpr int XB = x_buffers<MT, KH, RUN>();
@@ -346,7 +346,7 @@ __global__ __launch_bounds__(256 * KH) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int nr_all = min(a.rounds_per_split, (a.k - ks) / KR);
   const int nr0 = (nr_all + KH - 1) / KH;
   const int nr = team == 0 ? nr0 : nr_all - nr0;
-  SkinnyWave<R, ROUND, BF16, MT, NT, RUN, XB> w(a, tid, n0, ks + team * nr0 * KR);
+  SkinnyWave<R, RULE, BF16, MT, NT, RUN, XB> w(a, tid, n0, ks + team * nr0 * KR);
   if (nr > 0) w.run(nr, Xs[team][0], Xs[team][XB - 1]);
   const int lane = tid & 63;
   if constexpr (KH == 2) {
@@ -412,40 +412,40 @@ constexpr bool shape_ok() {
          KH * x_buffers<MT, KH, RUN>() * MT * RUN <= 16;
 }
 
-template <int R, int ROUND, int BF16, int MT, int NT, int KH, int RUN>
+template <int R, int RULE, int BF16, int MT, int NT, int KH, int RUN>
 hipError_t launch_k(const SkinnyArgs& sa, dim3 grid, hipStream_t s) {
   if constexpr (shape_ok<MT, KH, RUN>()) {
-    hipLaunchKernelGGL((skinny_kernel<R, ROUND, BF16, MT, NT, KH, RUN>), grid, dim3(256 * KH), 0, s, sa);
+    hipLaunchKernelGGL((skinny_kernel<R, RULE, BF16, MT, NT, KH, RUN>), grid, dim3(256 * KH), 0, s, sa);
     return hipGetLastError();
   } else {
     return hipErrorInvalidValue;
   }
 }
 
-template <int R, int ROUND, int BF16, int NT, int KH, int RUN>
+template <int R, int RULE, int BF16, int NT, int KH, int RUN>
 hipError_t launch_t(const SkinnyArgs& sa, int mt, dim3 grid, hipStream_t s) {
   switch (mt) {
-    case 1: return launch_k<R, ROUND, BF16, 1, NT, KH, RUN>(sa, grid, s);
-    case 2: return launch_k<R, ROUND, BF16, 2, NT, KH, RUN>(sa, grid, s);
-    case 3: return launch_k<R, ROUND, BF16, 3, NT, KH, RUN>(sa, grid, s);
-    default: return launch_k<R, ROUND, BF16, 4, NT, KH, RUN>(sa, grid, s);
+    case 1: return launch_k<R, RULE, BF16, 1, NT, KH, RUN>(sa, grid, s);
+    case 2: return launch_k<R, RULE, BF16, 2, NT, KH, RUN>(sa, grid, s);
+    case 3: return launch_k<R, RULE, BF16, 3, NT, KH, RUN>(sa, grid, s);
+    default: return launch_k<R, RULE, BF16, 4, NT, KH, RUN>(sa, grid, s);
   }
 }
 
 // 128-row workgroups (NT = 2) always take one run per round
-template <int R, int ROUND, int BF16>
+template <int R, int RULE, int BF16>
 hipError_t launch_b(const SkinnyArgs& sa, int mt, const SkinnyPlan& p, dim3 grid, hipStream_t s) {
-  if (p.nt == 2) return p.kh == 2 ? launch_t<R, ROUND, BF16, 2, 2, 1>(sa, mt, grid, s)
-                                  : launch_t<R, ROUND, BF16, 2, 1, 1>(sa, mt, grid, s);
-  if (p.run == 2) return p.kh == 2 ? launch_t<R, ROUND, BF16, 1, 2, 2>(sa, mt, grid, s)
-                                   : launch_t<R, ROUND, BF16, 1, 1, 2>(sa, mt, grid, s);
-  return p.kh == 2 ? launch_t<R, ROUND, BF16, 1, 2, 1>(sa, mt, grid, s)
-                   : launch_t<R, ROUND, BF16, 1, 1, 1>(sa, mt, grid, s);
+  if (p.nt == 2) return p.kh == 2 ? launch_t<R, RULE, BF16, 2, 2, 1>(sa, mt, grid, s)
+                                  : launch_t<R, RULE, BF16, 2, 1, 1>(sa, mt, grid, s);
+  if (p.run == 2) return p.kh == 2 ? launch_t<R, RULE, BF16, 1, 2, 2>(sa, mt, grid, s)
+                                   : launch_t<R, RULE, BF16, 1, 1, 2>(sa, mt, grid, s);
+  return p.kh == 2 ? launch_t<R, RULE, BF16, 1, 2, 1>(sa, mt, grid, s)
+                   : launch_t<R, RULE, BF16, 1, 1, 1>(sa, mt, grid, s);
 }
 
-template <int R, int ROUND>
+template <int R, int RULE>
 hipError_t launch_d(const SkinnyArgs& sa, int bf16, int mt, const SkinnyPlan& p, dim3 grid, hipStream_t s) {
-  return bf16 ? launch_b<R, ROUND, 1>(sa, mt, p, grid, s) : launch_b<R, ROUND, 0>(sa, mt, p, grid, s);
+  return bf16 ? launch_b<R, RULE, 1>(sa, mt, p, grid, s) : launch_b<R, RULE, 0>(sa, mt, p, grid, s);
 }
 
 }  // namespace
@@ -477,7 +477,7 @@ SkinnyPlan plan_skinny(int m, int n, int k, int group, int planes) {
 }
 
 size_t skinny_workspace_bytes(int m, int n, int k) {
-  if (!skinny_eligible(m, k)) return 0;
+  if (!skinny_shape(m, k)) return 0;
   // the k split depends on the run length, which depends on the group and
   // the width: size for the larger of the two plans
   const SkinnyPlan p1 = plan_skinny(m, n, k, 64, 1);
@@ -487,7 +487,8 @@ size_t skinny_workspace_bytes(int m, int n, int k) {
 }
 
 hipError_t launch_skinny(const LinearArgs& la, void* workspace, size_t workspace_bytes, hipStream_t s) {
-  SkinnyPlan p = plan_skinny(la.m, la.n, la.k, la.group, planes_needed(la.r, la.round_rule));
+  if (la.rule == kRuleExtra) return hipErrorInvalidValue;  // not a skinny rule (skinny_eligible)
+  SkinnyPlan p = plan_skinny(la.m, la.n, la.k, la.group, planes_needed(la.r, la.rule));
   if (p.splits > 1 && workspace_bytes < (size_t)p.splits * (size_t)la.m * (size_t)la.n * sizeof(float)) {
     p.splits = 1;
     p.rounds_per_split = la.k / (kRound * p.run);
@@ -509,7 +510,7 @@ hipError_t launch_skinny(const LinearArgs& la, void* workspace, size_t workspace
   hipError_t e;
 #define MQ_SK_CASE(RR)                                                                               \
   case RR:                                                                                           \
-    e = la.round_rule ? launch_d<RR, 1>(sa, la.bf16, mt, p, grid, s)                           \
+    e = la.rule ? launch_d<RR, 1>(sa, la.bf16, mt, p, grid, s)                           \
                       : launch_d<RR, 0>(sa, la.bf16, mt, p, grid, s);                          \
     break;
   switch (la.r) {

@@ -12,9 +12,10 @@ from dataclasses import dataclass, field
 import torch
 
 from . import _lib
-from ._lib import MQ_BF16, MQ_F16, MQ_F32, MQ_PREFIX, MQ_ROUND, MqError, NPLANES  # noqa: F401
+from ._lib import MQ_BF16, MQ_F16, MQ_F32, MQ_PREFIX, MQ_ROUND, MQ_ROUND_EXTRA, MqError, NPLANES  # noqa: F401
 
-RULES = {"prefix": MQ_PREFIX, "round": MQ_ROUND, MQ_PREFIX: MQ_PREFIX, MQ_ROUND: MQ_ROUND}
+RULES = {"prefix": MQ_PREFIX, "round": MQ_ROUND, "extra": MQ_ROUND_EXTRA,
+         MQ_PREFIX: MQ_PREFIX, MQ_ROUND: MQ_ROUND, MQ_ROUND_EXTRA: MQ_ROUND_EXTRA}
 _DTYPES = {torch.float16: MQ_F16, torch.bfloat16: MQ_BF16, torch.float32: MQ_F32}
 
 

@@ -25,6 +25,9 @@ pages rather than from the GPU's bit tricks:
 * Contraction (MatGPTQ section 4 "Fast Matryoshka Kernels"): Y = X W_D with
   the nn.Linear orientation, i.e. Y[m, n] = sum_k X[m, k] * w_hat[n, k],
   here in float64.
+* Extra-Precision MatQuant (MatQuant summary section 7 "Errata"): the
+  rounded slice without the clamp, S(q, r) = round(q / 2^(c-r)) * 2^(c-r),
+  which keeps 2^r + 1 values (unsigned 234 at r = 2 gives 256).
 * Mix'n'Match (MatQuant summary section 4.3): every layer matrix is sliced at
   its own width; the oracle applies the single-layer definition per call.
 
@@ -41,6 +44,7 @@ import numpy as np
 C_BITS = 8
 PREFIX = "prefix"   # MatGPTQ true-prefix slice (+ delta_r)
 ROUND = "round"     # MatQuant rounded and clamped slice
+EXTRA = "extra"     # Extra-Precision MatQuant: rounded, not clamped (2^r + 1 levels)
 
 
 # ----------------------------------------------------------------------------
@@ -93,6 +97,10 @@ def slice_code(q, r: int, rule: str, c: int = C_BITS, tie: str = "up") -> np.nda
         return slice_prefix(q, r, c)
     if rule == ROUND:
         return slice_round(q, r, c, tie)
+    if rule == EXTRA:
+        # MatQuant summary section 7 "Errata": the slice without the clamp keeps
+        # the extra value 2^r (2^r + 1 levels in all)
+        return slice_round_unclamped(q, r, c, tie)
     raise ValueError(rule)
 
 

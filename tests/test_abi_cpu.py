@@ -55,7 +55,8 @@ def test_planes_needed_table(L):
     # PREFIX reads r bits -> planes covering bits 2,3,4,6,8; ROUND reads r+1.
     assert [L.mq_planes_needed(r, 0) for r in (2, 3, 4, 6, 8)] == [1, 2, 3, 4, 5]
     assert [L.mq_planes_needed(r, 1) for r in (2, 3, 4, 6, 8)] == [2, 3, 4, 5, 5]
-    assert L.mq_planes_needed(5, 0) == -1 and L.mq_planes_needed(2, 7) == -1
+    assert [L.mq_planes_needed(r, 2) for r in (2, 3, 4, 6, 8)] == [2, 3, 4, 5, 5]
+    assert L.mq_planes_needed(5, 0) == -1 and L.mq_planes_needed(2, 7) == -1 and L.mq_planes_needed(2, 3) == -1
 
 
 def _packed(n=64, k=128, planes=(16, 32, 48, 64, 80)):
@@ -73,7 +74,7 @@ def _linear(L, x=4096, dt=1, m=1, w=None, r=4, rule=0, group=64, s=4096, z=8192,
 
 @pytest.mark.parametrize("kw,status", [
     (dict(r=5), 2), (dict(r=1), 2), (dict(r=9), 2),
-    (dict(rule=3), 8),
+    (dict(rule=3), 8), (dict(rule=-1), 8),
     (dict(group=32), 3), (dict(group=96), 3), (dict(group=0), 3),
     (dict(w=_packed(k=100)), 3), (dict(w=_packed(n=0)), 1), (dict(w=False), 1),
     (dict(m=-1), 1),

@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 
 TOL = 2e-3
 WIDTHS = [2, 3, 4, 6, 8]
-RULES = [O.PREFIX, O.ROUND]
+RULES = [O.PREFIX, O.ROUND, O.EXTRA]
 DEV = "cuda:0"
 
 
@@ -416,6 +416,18 @@ def test_llama_ffn_round_rule(mq, llama_ffn, r):
             x = synth.activations(synth.rng_for(2, 20 + r, m), m, lay.k, "f16")
             y = mq.linear(x.to(DEV), pk.truncated(r, O.ROUND), r, O.ROUND, 128, s, z)
             check_y(y, lay, x, r, O.ROUND, w64=w64)
+
+
+@pytest.mark.parametrize("r", [2, 3, 6])
+def test_llama_ffn_extra_precision(mq, llama_ffn, r):
+    # the unclamped slice (Extra-Precision MatQuant) at the full shapes: decode
+    # through the GEMV and a batch of 24 through the GEMM
+    for tid, lay, pk, s, z in llama_ffn:
+        w64 = w64_of(tid, lay, r, O.EXTRA)
+        for m in (1, 24):
+            x = synth.activations(synth.rng_for(2, 40 + r, m), m, lay.k, "f16")
+            y = mq.linear(x.to(DEV), pk.truncated(r, O.EXTRA), r, O.EXTRA, 128, s, z)
+            check_y(y, lay, x, r, O.EXTRA, w64=w64)
 
 
 @pytest.mark.parametrize("r", [2, 4, 6, 8])

@@ -85,7 +85,23 @@ def test_round_reads_exactly_r_plus_1_bits(r):
     assert np.array_equal(O.slice_prefix(ALLQ, r), O.slice_prefix(ALLQ & keep_r, r))
 
 
-@pytest.mark.parametrize("rule", [O.PREFIX, O.ROUND])
+@pytest.mark.parametrize("r", WIDTHS[:-1])
+def test_extra_is_the_round_slice_without_clamp(r):
+    # MatQuant summary section 7 "Errata": the unclamped variant keeps the value
+    # 2^r that the clamp removes; read off the binary digits: top r digits plus
+    # the (r+1)-th digit, no clamp.  2^r + 1 levels, the top one 2^c.
+    for q in ALLQ:
+        b = _bits(q)
+        pre = int(b[:r], 2) + int(b[r])
+        assert int(O.slice_code(q, r, O.EXTRA)) == pre
+        assert float(O.sliced_value(q, r, O.EXTRA)) == pre * 2 ** (8 - r)
+    vals = sorted(set(O.sliced_value(ALLQ, r, O.EXTRA).tolist()))
+    assert len(vals) == 2 ** r + 1 and vals[0] == 0.0 and vals[-1] == 256.0
+    differ = O.slice_code(ALLQ, r, O.EXTRA) != O.slice_code(ALLQ, r, O.ROUND)
+    assert np.all(O.slice_code(ALLQ, r, O.EXTRA)[differ] == 2 ** r)
+
+
+@pytest.mark.parametrize("rule", [O.PREFIX, O.ROUND, O.EXTRA])
 def test_identity_at_full_width(rule):
     assert np.array_equal(O.slice_code(ALLQ, 8, rule), ALLQ)
     assert np.array_equal(O.sliced_value(ALLQ, 8, rule), ALLQ.astype(float))
@@ -107,7 +123,7 @@ def test_nesting_and_monotonicity(r):
     for r2 in range(1, r + 1):
         assert np.array_equal(O.slice_prefix(O.slice_prefix(ALLQ, r) << (8 - r), r2),
                               O.slice_prefix(ALLQ, r2))
-    for rule in (O.PREFIX, O.ROUND):
+    for rule in (O.PREFIX, O.ROUND, O.EXTRA):
         v = O.sliced_value(ALLQ, r, rule)
         assert np.all(np.diff(v) >= 0)
 
@@ -160,7 +176,7 @@ def test_fp16_export_matches_library_rne():
     assert np.array_equal(O.export_f16(w).view(np.uint16), ref.view(np.uint16))
 
 
-@pytest.mark.parametrize("rule", [O.PREFIX, O.ROUND])
+@pytest.mark.parametrize("rule", [O.PREFIX, O.ROUND, O.EXTRA])
 @pytest.mark.parametrize("r", [2, 3, 4, 6, 8])
 def test_dequant_exact_in_fp32(r, rule):
     lay = synth.all_codes_layer(96, 1024, 128)
