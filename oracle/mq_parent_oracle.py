@@ -56,14 +56,16 @@ def candidate_shrink(i: int, grid_den: int) -> np.float32:
 
 def candidate_scale_zero(lo: np.ndarray, hi: np.ndarray, p: np.float32, c: int = C_BITS):
     """fp16 scale and integer zero point of the range [p*lo, p*hi] (lo <= 0 <= hi,
-    fp32).  A scale that rounds to zero in fp16 is replaced by 1."""
+    fp32).  A scale that rounds to zero in fp16 is replaced by 1; the zero
+    point is a non-negative integer (+0, never -0)."""
     qmax = F32(2 ** c - 1)
     lo_p = (p * lo).astype(F32)
     hi_p = (p * hi).astype(F32)
     s16 = ((hi_p - lo_p) / qmax).astype(F32).astype(np.float16)
     s16 = np.where(s16 == 0, np.float16(1), s16)
     s = s16.astype(F32)
-    z = np.clip(np.rint(-lo_p / s), 0, qmax).astype(F32)
+    # + 0 turns the -0 of an all-positive group (lo = 0) into the integer 0
+    z = np.clip(np.rint(-lo_p / s), 0, qmax).astype(F32) + F32(0)
     return s16, s, z
 
 

@@ -258,3 +258,13 @@ def test_centred_prefix_choice_is_the_nearest_code(widths, lams):
     far = np.abs(x - np.floor(x) - 0.5) > 1e-3
     assert np.array_equal(q[far], q_ref[far])
     assert np.all(np.abs(q.astype(int) - q_ref.astype(int)) <= 1)
+
+
+def test_zero_points_are_non_negative_integers():
+    """An all-positive group has lo = 0, so -lo * p is -0; the stored zero
+    point must be the integer 0 (+0)."""
+    w = np.abs(_layer(8, 256, seed=12))
+    s, z = P.search_scale_zero(w, 64, WIDTHS, LAMS, O.PREFIX, n_grid=10)
+    zb = z.view(np.uint16)
+    assert np.all(zb == 0)     # every group all positive -> zero point +0
+    assert np.all(z == np.rint(z)) and np.all(z >= 0)
