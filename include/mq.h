@@ -213,6 +213,44 @@ mq_status mq_dequant(const mq_packed* w, int32_t r, int32_t rule, int32_t group,
                      const uint16_t* scales, const uint16_t* zeros, int32_t out_dtype,
                      void* w_out, void* stream);
 
+/* Parent producer: the nested 8-bit parent of an fp32 weight matrix, without
+ * calibration data ("MatGPTQ: Efficient and Accurate Inference over Nested
+ * Quantized Models", section 3.2 points 1 and 2; Appendix A.2, Algorithms 1
+ * and 2; the Hessian-weighted error propagation of point 3 needs calibration
+ * activations and is not part of it).
+ *
+ *   w       fp32 [n, k] row-major (device), finite, with every group's
+ *           (max(0, max w) - min(0, min w)) / 255 below the fp16 maximum.
+ *   widths  host array of n_widths (1..5) distinct target widths in
+ *           {2, 3, 4, 6, 8}; lambdas: host array of their weights (finite,
+ *           >= 0), in the same order.
+ *   rule    the slice each width is reconstructed with (mq_rule).
+ *   codes   uint8 [n, k] (device), written: the parent codes.
+ *   scales, zeros: fp16 bit patterns [n, k/group] (device), written.
+ *
+ * Scale search (Algorithm 1): per group, candidate i = 0 .. n_grid - 1
+ * shrinks the range [min(0, min w), max(0, max w)] by p_i = 1 - i / grid_den
+ * (1 <= n_grid <= grid_den, n_grid <= 256) and takes s = fp16((p hi - p lo) /
+ * 255) (1 if that is zero) and z = clamp(rint(-p lo / s), 0, 255); every
+ * weight is coded to the nearest code clamp(rint(w / s) + z, 0, 255) and the
+ * candidate scores sum_j sum_r lambda_r (w_j - s (v_r(q_j) - z))^2.  The
+ * candidate with the smallest score (the first on ties) is kept.
+ * Code choice (Algorithm 2): per weight, the code q in 0..255 with the
+ * smallest sum_r lambda_r (w - s (v_r(q) - z))^2 (the first on ties).
+ * Decisions are fp32 comparisons with every operation rounded on its own, in
+ * this order: d = w - w_hat, t = lambda_r * (d * d), running sum over the
+ * widths in the given order (and, in the search, over the group's weights in
+ * index order, widths innermost).  The pages store the error matrix in fp32.
+ *
+ * Shape rules as for the layer, plus group <= 1024 (MQ_ESHAPE) and n * k <=
+ * 2^40 (MQ_ESIZE).  MQ_EINVAL for
+ * a bad n_widths, lambda, n_grid or grid_den; MQ_EWIDTH for a width outside
+ * {2,3,4,6,8} or repeated.  Two launches on `stream`; no workspace. */
+mq_status mq_produce_parent(const float* w, int32_t n, int32_t k, int32_t group, const int32_t* widths,
+                            const float* lambdas, int32_t n_widths, int32_t rule, int32_t n_grid,
+                            int32_t grid_den, uint8_t* codes, uint16_t* scales, uint16_t* zeros,
+                            void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,7 +24,7 @@ STATUS = {
 EXPORTS = (
     "mq_status_str", "mq_plane_bytes", "mq_planes_needed", "mq_pack_parent",
     "mq_linear_workspace_bytes", "mq_linear", "mq_linear_noalloc", "mq_linear_mixed", "mq_slice_codes",
-    "mq_dequant",
+    "mq_dequant", "mq_produce_parent",
 )
 
 # bytes of the static split-k scratch behind mq_linear_noalloc (MQ_NOALLOC_SCRATCH_BYTES)
@@ -83,6 +83,9 @@ def lib() -> ctypes.CDLL:
     L.mq_slice_codes.restype = ctypes.c_int
     L.mq_dequant.argtypes = [P, i32, i32, i32, vp, vp, i32, vp, vp]
     L.mq_dequant.restype = ctypes.c_int
+    L.mq_produce_parent.argtypes = [vp, i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_float), i32,
+                                    i32, i32, i32, vp, vp, vp, vp]
+    L.mq_produce_parent.restype = ctypes.c_int
     _lib = L
     return L
 

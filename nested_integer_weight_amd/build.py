@@ -18,7 +18,11 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmq.so")
-SOURCES = ["mq_api.hip", "mq_pack.hip", "mq_gemv.hip", "mq_gemm.hip", "mq_skinny.hip"]
+SOURCES = ["mq_api.hip", "mq_pack.hip", "mq_gemv.hip", "mq_gemm.hip", "mq_skinny.hip", "mq_produce.hip"]
+# The producer's decisions are fp32 comparisons with a fixed rounding of every
+# operation: correctly rounded division, fp32 denormals kept (contraction is
+# switched off inside the file).
+EXTRA = {"mq_produce.hip": ["-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-gpu-flush-denormals-to-zero"]}
 ARCH = os.environ.get("MQ_OFFLOAD_ARCH", "gfx950")
 
 COMMON = [
@@ -57,7 +61,7 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([hipcc, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([hipcc, *COMMON, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=min(len(cmds), 8)) as ex:
         outs = list(ex.map(_run, cmds))
     tmp = LIB + ".tmp"

@@ -360,4 +360,33 @@ mq_status mq_dequant(const mq_packed* w, int32_t r, int32_t rule, int32_t group,
              : MQ_EHIP;
 }
 
+mq_status mq_produce_parent(const float* w, int32_t n, int32_t k, int32_t group, const int32_t* widths,
+                            const float* lambdas, int32_t n_widths, int32_t rule, int32_t n_grid, int32_t grid_den,
+                            uint8_t* codes, uint16_t* scales, uint16_t* zeros, void* stream) {
+  if (!w || !codes || !scales || !zeros || !widths || !lambdas) return MQ_EINVAL;
+  mq_status st = check_shape(n, k);
+  if (st != MQ_OK) return st;
+  st = check_group(k, group);
+  if (st != MQ_OK) return st;
+  if (group > kMaxProduceGroup) return MQ_ESHAPE;
+  if ((uint64_t)n * (uint64_t)k > (1ull << 40)) return MQ_ESIZE;
+  if (!valid_rule(rule)) return MQ_ERULE;
+  if (n_widths < 1 || n_widths > kMaxProduceWidths) return MQ_EINVAL;
+  for (int i = 0; i < n_widths; ++i) {
+    if (!valid_width(widths[i])) return MQ_EWIDTH;
+    for (int j = 0; j < i; ++j)
+      if (widths[j] == widths[i]) return MQ_EWIDTH;
+    const float l = lambdas[i];
+    if (!(l >= 0.0f) || !(l <= 3.0e38f)) return MQ_EINVAL;  // finite, not negative, not NaN
+  }
+  if (grid_den < 1 || n_grid < 1 || n_grid > grid_den || n_grid > kMaxProduceGrid) return MQ_EINVAL;
+  if (!aligned16(w) || !aligned16(codes) || !aligned16(scales) || !aligned16(zeros)) return MQ_EALIGN;
+  int wv[kMaxProduceWidths];
+  for (int i = 0; i < n_widths; ++i) wv[i] = widths[i];
+  return launch_produce(w, n, k, group, wv, lambdas, n_widths, rule, n_grid, grid_den, codes, scales, zeros,
+                        static_cast<hipStream_t>(stream)) == hipSuccess
+             ? MQ_OK
+             : MQ_EHIP;
+}
+
 }  // extern "C"

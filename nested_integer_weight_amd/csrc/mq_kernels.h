@@ -71,4 +71,13 @@ GemmPlan plan_gemm(int m, int n, int k, size_t workspace_bytes);
 size_t gemm_workspace_bytes(int m, int n, int k);
 hipError_t launch_gemm(const LinearArgs& a, const GemmPlan& plan, void* workspace, hipStream_t s);
 
+// Parent producer: scale search, then the cross-width code choice, for
+// nr <= kMaxProduceWidths distinct widths (validated by the caller).
+constexpr int kMaxProduceWidths = 5;
+constexpr int kMaxProduceGroup = 1024;
+constexpr int kMaxProduceGrid = 256;
+hipError_t launch_produce(const float* w, int n, int k, int group, const int* widths, const float* lambdas, int nr,
+                          int rule, int n_grid, int grid_den, uint8_t* codes, uint16_t* scales, uint16_t* zeros,
+                          hipStream_t s);
+
 }  // namespace mq

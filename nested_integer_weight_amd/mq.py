@@ -228,3 +228,28 @@ def dequant(packed: Packed, r: int, rule, group: int, scales: torch.Tensor, zero
     _lib.check(_lib.lib().mq_dequant(ctypes.byref(packed.cstruct()), r, RULES[rule], group, _ptr(scales),
                                      _ptr(zeros), _DTYPES[dtype], _ptr(out), _stream(out.device)), "mq_dequant")
     return out
+
+
+def produce_parent(w: torch.Tensor, group: int, widths, lambdas, rule="prefix", n_grid: int = 80,
+                   grid_den: int = 100):
+    """Nested parent of fp32 weights w [n, k]: scale search and cross-width
+    code choice in the library.  Returns (codes uint8 [n, k], scales fp16
+    [n, k/group], zeros fp16 [n, k/group]) on w's device."""
+    _need_cuda(w, "w", torch.float32)
+    if w.dim() != 2:
+        raise ValueError("w must be [n, k]")
+    n, k = w.shape
+    widths = [int(r) for r in widths]
+    lambdas = [float(v) for v in lambdas]
+    if len(widths) != len(lambdas):
+        raise ValueError("widths and lambdas differ in length")
+    codes = torch.empty((n, k), dtype=torch.uint8, device=w.device)
+    g = max(k // group, 1) if group > 0 else 1
+    scales = torch.empty((n, g), dtype=torch.float16, device=w.device)
+    zeros = torch.empty((n, g), dtype=torch.float16, device=w.device)
+    wa = (ctypes.c_int32 * max(len(widths), 1))(*widths)
+    la = (ctypes.c_float * max(len(lambdas), 1))(*lambdas)
+    _lib.check(_lib.lib().mq_produce_parent(_ptr(w), n, k, group, wa, la, len(widths), RULES[rule], n_grid,
+                                            grid_den, _ptr(codes), _ptr(scales), _ptr(zeros), _stream(w.device)),
+               "mq_produce_parent")
+    return codes, scales, zeros

@@ -150,3 +150,26 @@ def test_noalloc_validation_before_any_hip_call(L):
     assert L.mq_linear_workspace_bytes(2048, 6144, 14336) > _lib.NOALLOC_SCRATCH_BYTES
     assert L.mq_linear_noalloc(args["x"], 2, 2048, ctypes.byref(w), 4, 0, 128, args["s"], args["z"], args["y"],
                                None) == 9
+
+
+def _produce(L, w=4096, n=64, k=256, group=64, widths=(3, 4, 8), lams=(1.0, 1.0, 1.0), nw=None, rule=0,
+             n_grid=80, grid_den=100, codes=8192, s=12288, z=16384):
+    wa = (ctypes.c_int32 * max(len(widths), 1))(*widths)
+    la = (ctypes.c_float * max(len(lams), 1))(*lams)
+    nw = len(widths) if nw is None else nw
+    return L.mq_produce_parent(w, n, k, group, wa, la, nw, rule, n_grid, grid_den, codes, s, z, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(w=0), 1), (dict(codes=0), 1), (dict(s=0), 1), (dict(z=0), 1),
+    (dict(n=0), 1), (dict(k=96), 3), (dict(group=96), 3), (dict(group=2048, k=4096), 3),
+    (dict(rule=3), 8),
+    (dict(widths=(3, 5, 8)), 2), (dict(widths=(3, 3, 8)), 2), (dict(widths=(1,), lams=(1.0,)), 2),
+    (dict(nw=0), 1), (dict(widths=(2, 3, 4, 6, 8, 8), lams=(1.0,) * 6), 1),
+    (dict(lams=(1.0, -1.0, 1.0)), 1), (dict(lams=(1.0, float("nan"), 1.0)), 1),
+    (dict(lams=(1.0, float("inf"), 1.0)), 1),
+    (dict(n_grid=0), 1), (dict(n_grid=101), 1), (dict(grid_den=0), 1), (dict(n_grid=300, grid_den=400), 1),
+    (dict(w=4100), 4), (dict(codes=8200), 4), (dict(s=12290), 4), (dict(n=1 << 20, k=1 << 21), 9),
+])
+def test_produce_validation(L, kw, status):
+    assert _produce(L, **kw) == status
