@@ -52,6 +52,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+# fp32 vector operations per second: the published 157.3 TFLOP/s fp32 vector
+# peak counts an FMA as two flops, i.e. 256 CUs x 4 SIMDs x 32 lanes per clock x
+# 2.4 GHz operations
+ALU_PEAK_OPS = 256 * 4 * 32 * 2.4e9
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 WIDTHS = (2, 3, 4, 6, 8)
 PREFILL_WIDTHS = (2, 4, 8)
@@ -102,6 +106,7 @@ def main():
     ap.add_argument("--no-mix", action="store_true", help="skip the 42-block Mix'n'Match stack lines")
     ap.add_argument("--no-pieces", action="store_true", help="skip the per-launch figures")
     ap.add_argument("--no-attn", action="store_true", help="skip the attention-projection lines")
+    ap.add_argument("--no-produce", action="store_true", help="skip the parent-producer lines")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -477,6 +482,43 @@ def main():
             del ys, calls, ref
         del blocks
 
+    # ---------------- parent producer (scale search + cross-width code choice) ----------------
+    # MatGPTQ's target set {3, 4, 8}, equal lambdas, 80 shrink candidates of the
+    # min-max range (p = 1 - i/100), on the three FFN matrices of the 8B model.
+    # Algorithmic fp32 operations per weight: per (weight, candidate) 3 (divide,
+    # round, add the zero point) + 6 per width (two to reconstruct, difference,
+    # square, weight, accumulate); per weight 5 per distinct level of each width
+    # + 2^8 x |R| (|R| - 1 additions and one comparison per code).
+    producer = None
+    if not args.no_produce:
+        pw, pl, pgrid, pden = [3, 4, 8], [1.0, 1.0, 1.0], 80, 100
+        levels = sum(2 ** r for r in pw)  # true prefix: 2^r levels per width (2^8 at r = 8)
+        ops_per_weight = pgrid * (3 + 6 * len(pw)) + 5 * levels + 256 * len(pw)
+        producer = {"widths": pw, "lambdas": pl, "n_grid": pgrid, "grid_den": pden, "group": GROUP,
+                    "rule": "prefix", "alg_ops_per_weight": ops_per_weight, "alu_peak_Tops": ALU_PEAK_OPS / 1e12}
+        tot_ms, tot_w = 0.0, 0
+        for i, (name, n, k) in enumerate(synth.LLAMA8B_FFN):
+            w = synth.device_weights(500 + i, n, k, dev)
+            mq.produce_parent(w, GROUP, pw, pl, "prefix", pgrid, pden)
+            torch.cuda.synchronize()
+            reps = 3
+            a_, b_ = ev(), ev()
+            a_.record(stream)
+            for _ in range(reps):
+                mq.produce_parent(w, GROUP, pw, pl, "prefix", pgrid, pden)
+            b_.record(stream)
+            torch.cuda.synchronize()
+            ms = a_.elapsed_time(b_) / reps
+            tot_ms += ms
+            tot_w += n * k
+            producer[name] = {"ms": round(ms, 3), "Gweights/s": round(n * k / (ms * 1e-3) / 1e9, 3)}
+            del w
+        producer["ffn_ms"] = round(tot_ms, 3)
+        producer["Gweights/s"] = round(tot_w / (tot_ms * 1e-3) / 1e9, 3)
+        producer["alu_frac"] = round(tot_w * ops_per_weight / (tot_ms * 1e-3) / ALU_PEAK_OPS, 4)
+        log(f"[bench] producer: 8B FFN (3 matrices) in {tot_ms:.2f} ms, {producer['Gweights/s']} Gweights/s, "
+            f"{producer['alu_frac'] * 100:.1f}% of the fp32 VALU issue rate")
+
     # ---------------- reference: device copies at the decode launch sizes ----------------
     # torch's device copy over a ring of buffers (> 1 GiB per pass): read and
     # write bytes over the copy time, the streaming rate one launch of that size
@@ -574,6 +616,7 @@ def main():
         "per_r": per_r,
         "attention": attn,
         "copy_reference": copy_ref,
+        "producer": producer,
         "eager": eager,
         "skinny": skinny,
         "mixnmatch": mix,

@@ -132,13 +132,11 @@ def mixnmatch_widths(n_blocks: int = GEMMA9B_BLOCKS, seed: int = 0) -> list[int]
     return [int(v) for v in np.random.default_rng(seed).permutation(base)]
 
 
-def device_parent(seed: int, n: int, k: int, group: int, device, std: float = 0.02,
-                  outlier_frac: float = 1e-3, outlier_mult: float = 10.0, c: int = C_BITS):
-    """The same recipe as `make_layer` + `minmax_parent`, drawn on `device` with
-    a seeded torch generator (for workloads too large to draw on the host):
-    W ~ N(0, std^2) fp32 with round(outlier_frac*n*k) entries x outlier_mult,
-    then per-group min-max quantization in fp32 (RNE), fp16 scale, integer zero.
-    Returns (q uint8 [n,k], scales fp16 [n,k/group], zeros fp16 [n,k/group])."""
+def device_weights(seed: int, n: int, k: int, device, std: float = 0.02, outlier_frac: float = 1e-3,
+                   outlier_mult: float = 10.0):
+    """fp32 [n, k] W ~ N(0, std^2) drawn on `device` with a seeded torch
+    generator, with round(outlier_frac*n*k) entries (drawn with replacement)
+    multiplied by outlier_mult."""
     import torch
     g = torch.Generator(device=device)
     g.manual_seed(int(seed))
@@ -147,6 +145,18 @@ def device_parent(seed: int, n: int, k: int, group: int, device, std: float = 0.
     if n_out:
         idx = torch.randint(0, n * k, (n_out,), generator=g, device=device)
         w.view(-1)[idx] *= outlier_mult
+    return w
+
+
+def device_parent(seed: int, n: int, k: int, group: int, device, std: float = 0.02,
+                  outlier_frac: float = 1e-3, outlier_mult: float = 10.0, c: int = C_BITS):
+    """The same recipe as `make_layer` + `minmax_parent`, drawn on `device` with
+    a seeded torch generator (for workloads too large to draw on the host):
+    W ~ N(0, std^2) fp32 with round(outlier_frac*n*k) entries x outlier_mult,
+    then per-group min-max quantization in fp32 (RNE), fp16 scale, integer zero.
+    Returns (q uint8 [n,k], scales fp16 [n,k/group], zeros fp16 [n,k/group])."""
+    import torch
+    w = device_weights(seed, n, k, device, std, outlier_frac, outlier_mult)
     qmax = float(2 ** c - 1)
     wg = w.view(n, k // group, group)
     lo = torch.clamp(wg.amin(dim=-1), max=0.0)
