@@ -126,8 +126,10 @@ typedef struct {
   void* y;
 } mq_call;
 
-/* Human-readable name of a status (static string, never NULL). */
-const char* mq_status_str(mq_status s);
+/* Human-readable name of a status value (static string, never NULL;
+ * "MQ_UNKNOWN" for a value that is not an mq_status).  Takes a plain int so
+ * that any value may be passed. */
+const char* mq_status_str(int32_t s);
 
 /* Bytes of plane `plane` (0..4) for an [n, k] parent: n*k*bits/8, with
  * bits = 2,1,1,2,2.  Returns 0 for an invalid plane index or shape.  Pure,

@@ -196,7 +196,7 @@ mq_status scratch_on(int dev, void** out) {
 
 extern "C" {
 
-const char* mq_status_str(mq_status s) {
+const char* mq_status_str(int32_t s) {
   switch (s) {
     case MQ_OK: return "MQ_OK";
     case MQ_EINVAL: return "MQ_EINVAL: null pointer or invalid size";
