@@ -397,38 +397,51 @@ def main():
             log(f"[bench] prefill r={r}: {tf:.1f} TFLOP/s")
 
     # ---------------- skinny decode batches (M = 8..64, fp16) ----------------
+    # gate, up and down (separate outputs) through mq_linear_mixed, so calls of
+    # one launch shape share a launch; figures are per call (a third of a step)
     skinny = None
     if not args.no_skinny:
         skinny = {}
         for m in (8, 16, 32, 64):
             xs_m = {k: synth.activations(synth.rng_for(3, m, k), m, k, "f16").to(dev) for k in (4096, 14336)}
-            ys_m = {n: torch.empty((m, n), dtype=torch.float16, device=dev) for n in (4096, 14336)}
+            # one output per matrix (gate and up must not share one, or they could not share a launch)
+            ys_m = {mt["name"]: torch.empty((m, mt["n"]), dtype=torch.float16, device=dev) for mt in mats}
             for r in (2, 3, 4, 8):
                 def sk_calls(it):
                     c = it % ring
                     return [mq.Call(x=xs_m[mt["k"]], packed=mt["copies"][c][0].truncated(r), r=r, rule="prefix",
                                     group=GROUP, scales=mt["copies"][c][1], zeros=mt["copies"][c][2],
-                                    out=ys_m[mt["n"]]) for mt in mats]
-                for i in range(3):
-                    mq.linear_mixed(sk_calls(i))
-                torch.cuda.synchronize()
+                                    out=ys_m[mt["name"]]) for mt in mats]
+                def one_by_one(cl):
+                    for c in cl:
+                        mq.linear(c.x, c.packed, c.r, c.rule, c.group, c.scales, c.zeros, out=c.out)
+
                 iters = max(ring, math.ceil(MIN_LAUNCHES / len(mats)))
-                a_, b_ = ev(), ev()
-                a_.record(stream)
-                for i in range(iters):
-                    mq.linear_mixed(sk_calls(3 + i))
-                b_.record(stream)
-                torch.cuda.synchronize()
-                us = a_.elapsed_time(b_) * 1e3 / (iters * len(mats))
+                per_call = {}
+                for mode, issue in (("shared", mq.linear_mixed), ("one_by_one", one_by_one)):
+                    for i in range(3):
+                        issue(sk_calls(i))
+                    torch.cuda.synchronize()
+                    a_, b_ = ev(), ev()
+                    a_.record(stream)
+                    for i in range(iters):
+                        issue(sk_calls(3 + i))
+                    b_.record(stream)
+                    torch.cuda.synchronize()
+                    per_call[mode] = a_.elapsed_time(b_) * 1e3 / (iters * len(mats))
+                us = per_call["shared"]
                 byt = sum(alg_bytes(m, mt["n"], mt["k"], r) for mt in mats) / len(mats)
                 fl = 2.0 * m * sum(mt["n"] * mt["k"] for mt in mats) / len(mats)
                 t_hbm = byt / (HBM_PEAK_GBS * 1e9)
                 t_mfma = fl / (BF16_MFMA_PEAK_TFLOPS * 1e12)
-                skinny[f"m{m}_r{r}"] = {"us_per_launch": round(us, 2), "GB/s": round(byt / (us * 1e-6) / 1e9, 1),
+                skinny[f"m{m}_r{r}"] = {"us_per_call": round(us, 2),
+                                        "us_per_call_one_launch_each": round(per_call["one_by_one"], 2),
+                                        "GB/s": round(byt / (us * 1e-6) / 1e9, 1),
                                         "TFLOP/s": round(fl / (us * 1e-6) / 1e12, 1),
                                         "roofline_frac": round(max(t_hbm, t_mfma) / (us * 1e-6), 4)}
-            log(f"[bench] skinny m={m}: " + ", ".join(f"r{r} {skinny[f'm{m}_r{r}']['us_per_launch']}us"
-                                                       for r in (2, 3, 4, 8)))
+            log(f"[bench] skinny m={m} (us per call, shared launches / one launch each): " +
+                ", ".join(f"r{r} {skinny[f'm{m}_r{r}']['us_per_call']} / "
+                          f"{skinny[f'm{m}_r{r}']['us_per_call_one_launch_each']}" for r in (2, 3, 4, 8)))
 
     # ---------------- Mix'n'Match stack: 42 Gemma-2-9B FFN blocks ----------------
     mix = None

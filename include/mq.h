@@ -198,11 +198,21 @@ mq_status mq_linear_noalloc(const void* x, int32_t x_dtype, int32_t m, const mq_
  * m <= 4, bf16 x with m == 1, k <= 16384) with the same m, width, rule and
  * dtype joins one launch (up to 32 calls of any shape, e.g. the gate, up and
  * down projections of a decode step, or the projections of several
- * Mix'n'Match blocks); the other calls run one by one.  The results are those
- * of issuing the calls in order, bit for bit.  A launch error reports the
- * first call of its launch. */
+ * Mix'n'Match blocks); skinny-path calls (see mq_linear) with the same m,
+ * width, rule, dtype and planned workgroup shape join one launch too (up to
+ * 8 calls), each keeping its own k split as long as the workspace holds all
+ * of them (mq_linear_mixed_workspace_bytes); the other calls run one by one.
+ * The results are those of issuing the calls in order, bit for bit.  A launch
+ * error reports the first call of its launch. */
 mq_status mq_linear_mixed(const mq_call* calls, int32_t n_calls, void* workspace,
                           size_t workspace_bytes, int32_t* failed_call, void* stream);
+
+/* Workspace bytes with which mq_linear_mixed gives every call of `calls` the
+ * k split it has as a single call, also where several split calls share a
+ * launch: the larger of the single-call need and the 256-byte-aligned sum over
+ * the calls that take the skinny MFMA path.  Pure, host only (reads the call
+ * structs, not the device buffers); invalid entries count as 0. */
+size_t mq_linear_mixed_workspace_bytes(const mq_call* calls, int32_t n_calls);
 
 /* Test support (same device functions as the GEMMs).
  * mq_slice_codes: codes_out [n, k] uint8 = the r-bit code (0..2^r - 1; 0..2^r

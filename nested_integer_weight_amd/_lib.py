@@ -24,7 +24,7 @@ STATUS = {
 EXPORTS = (
     "mq_status_str", "mq_plane_bytes", "mq_planes_needed", "mq_pack_parent",
     "mq_linear_workspace_bytes", "mq_linear", "mq_linear_noalloc", "mq_linear_mixed", "mq_slice_codes",
-    "mq_dequant", "mq_produce_parent",
+    "mq_dequant", "mq_produce_parent", "mq_linear_mixed_workspace_bytes",
 )
 
 # bytes of the static split-k scratch behind mq_linear_noalloc (MQ_NOALLOC_SCRATCH_BYTES)
@@ -79,6 +79,8 @@ def lib() -> ctypes.CDLL:
     L.mq_linear_noalloc.restype = ctypes.c_int
     L.mq_linear_mixed.argtypes = [ctypes.POINTER(MqCall), i32, vp, sz, ctypes.POINTER(i32), vp]
     L.mq_linear_mixed.restype = ctypes.c_int
+    L.mq_linear_mixed_workspace_bytes.argtypes = [ctypes.POINTER(MqCall), i32]
+    L.mq_linear_mixed_workspace_bytes.restype = sz
     L.mq_slice_codes.argtypes = [P, i32, i32, vp, vp]
     L.mq_slice_codes.restype = ctypes.c_int
     L.mq_dequant.argtypes = [P, i32, i32, i32, vp, vp, i32, vp, vp]

@@ -138,6 +138,7 @@ bool same_gemv_class(const mq_call& c, const mq_call& d) {
   return c.m == d.m && c.r == d.r && c.rule == d.rule && c.x_dtype == d.x_dtype;
 }
 bool gemv_call(const mq_call& c) { return c.m > 0 && gemv_eligible(c.m, c.w->k, c.x_dtype == MQ_BF16); }
+bool skinny_call(const mq_call& c) { return c.m > 0 && !gemv_call(c) && skinny_eligible(c.m, c.w->k, c.rule); }
 
 LinearArgs call_args(const mq_call& c, const PlanePtrs& pl) {
   LinearArgs a;
@@ -250,6 +251,20 @@ size_t mq_linear_workspace_bytes(int32_t m, int32_t n, int32_t k) {
   return gemm_workspace_bytes(m, n, k);
 }
 
+size_t mq_linear_mixed_workspace_bytes(const mq_call* calls, int32_t n_calls) {
+  if (!calls || n_calls <= 0) return 0;
+  size_t single = 0, skinny_sum = 0;
+  for (int32_t i = 0; i < n_calls; ++i) {
+    const mq_call& c = calls[i];
+    if (!c.w || c.m <= 0 || c.w->n <= 0 || c.w->k <= 0 || c.group <= 0 || !valid_width(c.r) || !valid_rule(c.rule))
+      continue;
+    const size_t one = mq_linear_workspace_bytes(c.m, c.w->n, c.w->k);
+    if (one > single) single = one;
+    if (skinny_call(c)) skinny_sum = ws_align(skinny_sum) + skinny_call_workspace(call_args(c, planes_of(c)));
+  }
+  return single > skinny_sum ? single : skinny_sum;
+}
+
 mq_status mq_linear(const void* x, int32_t x_dtype, int32_t m, const mq_packed* w, int32_t r, int32_t rule,
                     int32_t group, const uint16_t* scales, const uint16_t* zeros, void* y, void* workspace,
                     size_t workspace_bytes, void* stream) {
@@ -294,8 +309,9 @@ mq_status mq_linear_mixed(const mq_call* calls, int32_t n_calls, void* workspace
   }
   // Runs of consecutive, pairwise independent calls: inside a run the order
   // does not matter, so every GEMV-eligible call of one class (m, width,
-  // rule, dtype) goes into one launch, whatever its shape, and the other calls
-  // run one by one.  Runs follow each other in stream order.
+  // rule, dtype) goes into one launch, whatever its shape, skinny calls of
+  // one launch shape share launches, and the other calls run one by one.
+  // Runs follow each other in stream order.
   for (int32_t i = 0; i < n_calls;) {
     int32_t j = i + 1;
     while (j < n_calls && j - i < kWindow) {
@@ -318,6 +334,33 @@ mq_status mq_linear_mixed(const mq_call* calls, int32_t n_calls, void* workspace
           done[u - i] = true;
         }
         st = launch_gemv_multi(la, nl, static_cast<hipStream_t>(stream)) == hipSuccess ? MQ_OK : MQ_EHIP;
+      } else if (skinny_call(c)) {
+        // skinny calls of one launch shape share a launch; a call with a k
+        // split joins only where its part of the workspace fits (or where it
+        // would not fit even alone), so every call keeps the plan it has as a
+        // single call and the results are those of single calls
+        const bool ws_ok = workspace && aligned16(workspace);
+        const size_t ws_b = ws_ok ? workspace_bytes : 0;
+        LinearArgs la[kSkinnyMaxCalls];
+        const LinearArgs a0 = call_args(c, planes_of(c));
+        int nl = 0;
+        size_t used = 0;
+        for (int32_t u = t; u < j && nl < kSkinnyMaxCalls; ++u) {
+          if (done[u - i] || !skinny_call(calls[u])) continue;
+          const LinearArgs au = call_args(calls[u], planes_of(calls[u]));
+          if (!same_skinny_launch(a0, au)) continue;
+          const size_t need = skinny_call_workspace(au);
+          if (need && need <= ws_b) {
+            if (ws_align(used) + need > ws_b) continue;  // joins a later launch
+            used = ws_align(used) + need;
+          }
+          la[nl++] = au;
+          done[u - i] = true;
+        }
+        st = launch_skinny_multi(la, nl, ws_ok ? workspace : nullptr, ws_b, static_cast<hipStream_t>(stream)) ==
+                     hipSuccess
+                 ? MQ_OK
+                 : MQ_EHIP;
       } else {
         done[t - i] = true;
         st = run_linear(c.x, c.x_dtype, c.m, c.w, c.r, c.rule, c.group, c.scales, c.zeros, c.y, workspace,

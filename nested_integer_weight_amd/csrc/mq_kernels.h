@@ -58,6 +58,18 @@ struct SkinnyPlan {
 SkinnyPlan plan_skinny(int m, int n, int k, int group, int planes);
 size_t skinny_workspace_bytes(int m, int n, int k);
 hipError_t launch_skinny(const LinearArgs& a, void* workspace, size_t workspace_bytes, hipStream_t s);
+// Up to kSkinnyMaxCalls independent skinny calls of one launch shape (same m,
+// width, rule, dtype and planned row tiles, teams and run length) in one
+// launch.  Each call keeps its own plan; a call with a k split takes the next
+// 256-byte-aligned part of the workspace (and runs unsplit when that part
+// does not fit, as a single call would), and its partial sums are reduced
+// after the launch.
+constexpr int kSkinnyMaxCalls = 8;
+__host__ inline size_t ws_align(size_t b) { return (b + 255) & ~(size_t)255; }
+bool same_skinny_launch(const LinearArgs& a, const LinearArgs& b);
+size_t skinny_call_workspace(const LinearArgs& a);  // bytes of its k split, 0 when it does not split
+hipError_t launch_skinny_multi(const LinearArgs* a, int ncalls, void* workspace, size_t workspace_bytes,
+                               hipStream_t s);
 
 // fixed-order sum of fp32 split-k partials ws[splits][mn] rounded once into y (fp16 or bf16)
 hipError_t launch_splitk_reduce(const float* ws, int splits, size_t mn, void* y, int bf16, hipStream_t s);

@@ -29,9 +29,12 @@
 //   bf16: exact in fp32 (v * s + (delta - z) * s), then one RNE to bf16.
 // Accumulation is fp32 in the MFMA.
 //
-// Split-k: blockIdx.y picks a k range; with more than one range the fp32
-// partial tiles go to workspace[split][m][n] and the fixed-order reduction
+// Split-k: a workgroup's flat index picks its call, then its row block and k
+// range there; with more than one range the fp32 partial tiles go to the
+// call's part of the workspace, [split][m][n], and the fixed-order reduction
 // kernel of the GEMM path sums them, so results stay deterministic.
+// Independent calls of one launch shape share a launch (one ramp and drain).
+
 #include "mq_common.h"
 #include "mq_kernels.h"
 
@@ -64,6 +67,17 @@ struct SkinnyArgs {
   int m, n, k, group;
   int rounds_per_split;
   int to_workspace;
+};
+
+// The calls of one launch: call i owns the flat workgroups blk0[i] ..
+// blk0[i] + gx[i] * splits_i - 1, row block fastest.  All calls share the
+// kernel's template shape (width, rule, dtype, m tiles, row tiles, teams,
+// run length).
+struct SkinnyLaunch {
+  SkinnyArgs c[kSkinnyMaxCalls];
+  int gx[kSkinnyMaxCalls];
+  int blk0[kSkinnyMaxCalls];
+  int ncalls;
 };
 
 template <int BF16>
@@ -335,14 +349,21 @@ constexpr int x_buffers() { return (KH == 2 && RUN == 2 && MT >= 3) ? 1 : 2; }
 // Two waves per SIMD is enough to cover the latency with the prefetch above;
 // asking for more would make the compiler spill the staging registers.
 template <int R, int RULE, int BF16, int MT, int NT, int KH, int RUN>
-__global__ __launch_bounds__(256 * KH) __attribute__((amdgpu_waves_per_eu(2, 2))) void skinny_kernel(SkinnyArgs a) {
+__global__ __launch_bounds__(256 * KH) __attribute__((amdgpu_waves_per_eu(2, 2))) void skinny_kernel(SkinnyLaunch L) {
   constexpr int KR = kRound * RUN;
   constexpr int XB = x_buffers<MT, KH, RUN>();
   __shared__ u32x4 Xs[KH][XB][MT * 8 * RUN * 64];
+  // the call this workgroup serves, and its row block and k range there
+  int ci = 0;
+  while (ci + 1 < L.ncalls && (int)blockIdx.x >= L.blk0[ci + 1]) ++ci;
+  const SkinnyArgs& a = L.c[ci];
+  const int local = (int)blockIdx.x - L.blk0[ci];
+  const int by = local / L.gx[ci];
+  const int bx = local - by * L.gx[ci];
   const int team = KH == 2 ? (int)(threadIdx.x >> 8) : 0;
   const int tid = threadIdx.x & 255;
-  const int n0 = blockIdx.x * cols_per_block<NT>();
-  const int ks = blockIdx.y * a.rounds_per_split * KR;
+  const int n0 = bx * cols_per_block<NT>();
+  const int ks = by * a.rounds_per_split * KR;
   const int nr_all = min(a.rounds_per_split, (a.k - ks) / KR);
   const int nr0 = (nr_all + KH - 1) / KH;
   const int nr = team == 0 ? nr0 : nr_all - nr0;
@@ -386,7 +407,7 @@ __global__ __launch_bounds__(256 * KH) __attribute__((amdgpu_waves_per_eu(2, 2))
         if (mm < a.m && nn < a.n) {
           const float val = w.acc[mt][t][v];
           if (a.to_workspace) {
-            static_cast<float*>(a.y)[((size_t)blockIdx.y * a.m + mm) * a.n + nn] = val;
+            static_cast<float*>(a.y)[((size_t)by * a.m + mm) * a.n + nn] = val;
           } else {
             uint16_t* y = static_cast<uint16_t*>(a.y) + (size_t)mm * a.n + nn;
             *y = (uint16_t)((BF16 ? pack_bf16x2(val, 0.f) : pack_f16x2(val, 0.f)) & 0xFFFFu);
@@ -413,7 +434,7 @@ constexpr bool shape_ok() {
 }
 
 template <int R, int RULE, int BF16, int MT, int NT, int KH, int RUN>
-hipError_t launch_k(const SkinnyArgs& sa, dim3 grid, hipStream_t s) {
+hipError_t launch_k(const SkinnyLaunch& sa, dim3 grid, hipStream_t s) {
   if constexpr (shape_ok<MT, KH, RUN>()) {
     hipLaunchKernelGGL((skinny_kernel<R, RULE, BF16, MT, NT, KH, RUN>), grid, dim3(256 * KH), 0, s, sa);
     return hipGetLastError();
@@ -423,7 +444,7 @@ hipError_t launch_k(const SkinnyArgs& sa, dim3 grid, hipStream_t s) {
 }
 
 template <int R, int RULE, int BF16, int NT, int KH, int RUN>
-hipError_t launch_t(const SkinnyArgs& sa, int mt, dim3 grid, hipStream_t s) {
+hipError_t launch_t(const SkinnyLaunch& sa, int mt, dim3 grid, hipStream_t s) {
   switch (mt) {
     case 1: return launch_k<R, RULE, BF16, 1, NT, KH, RUN>(sa, grid, s);
     case 2: return launch_k<R, RULE, BF16, 2, NT, KH, RUN>(sa, grid, s);
@@ -434,7 +455,7 @@ hipError_t launch_t(const SkinnyArgs& sa, int mt, dim3 grid, hipStream_t s) {
 
 // 128-row workgroups (NT = 2) always take one run per round
 template <int R, int RULE, int BF16>
-hipError_t launch_b(const SkinnyArgs& sa, int mt, const SkinnyPlan& p, dim3 grid, hipStream_t s) {
+hipError_t launch_b(const SkinnyLaunch& sa, int mt, const SkinnyPlan& p, dim3 grid, hipStream_t s) {
   if (p.nt == 2) return p.kh == 2 ? launch_t<R, RULE, BF16, 2, 2, 1>(sa, mt, grid, s)
                                   : launch_t<R, RULE, BF16, 2, 1, 1>(sa, mt, grid, s);
   if (p.run == 2) return p.kh == 2 ? launch_t<R, RULE, BF16, 1, 2, 2>(sa, mt, grid, s)
@@ -444,7 +465,7 @@ hipError_t launch_b(const SkinnyArgs& sa, int mt, const SkinnyPlan& p, dim3 grid
 }
 
 template <int R, int RULE>
-hipError_t launch_d(const SkinnyArgs& sa, int bf16, int mt, const SkinnyPlan& p, dim3 grid, hipStream_t s) {
+hipError_t launch_d(const SkinnyLaunch& sa, int bf16, int mt, const SkinnyPlan& p, dim3 grid, hipStream_t s) {
   return bf16 ? launch_b<R, RULE, 1>(sa, mt, p, grid, s) : launch_b<R, RULE, 0>(sa, mt, p, grid, s);
 }
 
@@ -486,34 +507,68 @@ size_t skinny_workspace_bytes(int m, int n, int k) {
   return splits > 1 ? (size_t)splits * (size_t)m * (size_t)n * sizeof(float) : 0;
 }
 
-hipError_t launch_skinny(const LinearArgs& la, void* workspace, size_t workspace_bytes, hipStream_t s) {
-  if (la.rule == kRuleExtra) return hipErrorInvalidValue;  // not a skinny rule (skinny_eligible)
-  SkinnyPlan p = plan_skinny(la.m, la.n, la.k, la.group, planes_needed(la.r, la.rule));
-  if (p.splits > 1 && workspace_bytes < (size_t)p.splits * (size_t)la.m * (size_t)la.n * sizeof(float)) {
-    p.splits = 1;
-    p.rounds_per_split = la.k / (kRound * p.run);
+SkinnyPlan plan_skinny_call(const LinearArgs& la) {
+  return plan_skinny(la.m, la.n, la.k, la.group, planes_needed(la.r, la.rule));
+}
+
+size_t skinny_call_workspace(const LinearArgs& la) {
+  const SkinnyPlan p = plan_skinny_call(la);
+  return p.splits > 1 ? (size_t)p.splits * (size_t)la.m * (size_t)la.n * sizeof(float) : 0;
+}
+
+bool same_skinny_launch(const LinearArgs& a, const LinearArgs& b) {
+  if (a.m != b.m || a.r != b.r || a.rule != b.rule || a.bf16 != b.bf16) return false;
+  const SkinnyPlan p = plan_skinny_call(a), q = plan_skinny_call(b);
+  return p.nt == q.nt && p.kh == q.kh && p.run == q.run;
+}
+
+hipError_t launch_skinny_multi(const LinearArgs* la, int ncalls, void* workspace, size_t workspace_bytes,
+                               hipStream_t s) {
+  if (ncalls < 1 || ncalls > kSkinnyMaxCalls) return hipErrorInvalidValue;
+  for (int i = 0; i < ncalls; ++i)
+    if (la[i].rule == kRuleExtra || !same_skinny_launch(la[0], la[i])) return hipErrorInvalidValue;
+  SkinnyLaunch L;
+  SkinnyPlan plan[kSkinnyMaxCalls];
+  size_t ws_off[kSkinnyMaxCalls];
+  size_t used = 0;
+  int blocks = 0;
+  for (int i = 0; i < ncalls; ++i) {
+    SkinnyPlan p = plan_skinny_call(la[i]);
+    const size_t need = p.splits > 1 ? (size_t)p.splits * (size_t)la[i].m * (size_t)la[i].n * sizeof(float) : 0;
+    ws_off[i] = ws_align(used);
+    if (need && (!workspace || ws_off[i] + need > workspace_bytes)) {
+      // not enough workspace for this call's k split: one range
+      p.splits = 1;
+      p.rounds_per_split = la[i].k / (kRound * p.run);
+    }
+    if (p.splits > 1) used = ws_off[i] + need;
+    plan[i] = p;
+    SkinnyArgs& sa = L.c[i];
+    sa.x = static_cast<const uint16_t*>(la[i].x);
+    sa.pl = la[i].pl;
+    sa.scales = la[i].scales;
+    sa.zeros = la[i].zeros;
+    sa.m = la[i].m;
+    sa.n = la[i].n;
+    sa.k = la[i].k;
+    sa.group = la[i].group;
+    sa.rounds_per_split = p.rounds_per_split;
+    sa.to_workspace = p.splits > 1;
+    sa.y = p.splits > 1 ? static_cast<void*>(static_cast<char*>(workspace) + ws_off[i]) : la[i].y;
+    L.gx[i] = cdiv(la[i].n, p.nt == 1 ? cols_per_block<1>() : cols_per_block<2>());
+    L.blk0[i] = blocks;
+    blocks += L.gx[i] * p.splits;
   }
-  SkinnyArgs sa;
-  sa.x = static_cast<const uint16_t*>(la.x);
-  sa.pl = la.pl;
-  sa.scales = la.scales;
-  sa.zeros = la.zeros;
-  sa.m = la.m;
-  sa.n = la.n;
-  sa.k = la.k;
-  sa.group = la.group;
-  sa.rounds_per_split = p.rounds_per_split;
-  sa.to_workspace = p.splits > 1;
-  sa.y = p.splits > 1 ? workspace : la.y;
-  const int mt = cdiv(la.m, 16);
-  const dim3 grid((unsigned)cdiv(la.n, p.nt == 1 ? cols_per_block<1>() : cols_per_block<2>()), (unsigned)p.splits);
+  L.ncalls = ncalls;
+  const int mt = cdiv(la[0].m, 16);
+  const dim3 grid((unsigned)blocks);
   hipError_t e;
-#define MQ_SK_CASE(RR)                                                                               \
-  case RR:                                                                                           \
-    e = la.rule ? launch_d<RR, 1>(sa, la.bf16, mt, p, grid, s)                           \
-                      : launch_d<RR, 0>(sa, la.bf16, mt, p, grid, s);                          \
+#define MQ_SK_CASE(RR)                                                                  \
+  case RR:                                                                              \
+    e = la[0].rule ? launch_d<RR, 1>(L, la[0].bf16, mt, plan[0], grid, s)               \
+                   : launch_d<RR, 0>(L, la[0].bf16, mt, plan[0], grid, s);              \
     break;
-  switch (la.r) {
+  switch (la[0].r) {
     MQ_SK_CASE(2)
     MQ_SK_CASE(3)
     MQ_SK_CASE(4)
@@ -522,9 +577,16 @@ hipError_t launch_skinny(const LinearArgs& la, void* workspace, size_t workspace
     default: return hipErrorInvalidValue;
   }
 #undef MQ_SK_CASE
-  if (e != hipSuccess || p.splits == 1) return e;
-  return launch_splitk_reduce(static_cast<const float*>(workspace), p.splits, (size_t)la.m * (size_t)la.n, la.y,
-                              la.bf16, s);
+  if (e != hipSuccess) return e;
+  for (int i = 0; i < ncalls && e == hipSuccess; ++i)
+    if (plan[i].splits > 1)
+      e = launch_splitk_reduce(static_cast<const float*>(L.c[i].y), plan[i].splits,
+                               (size_t)la[i].m * (size_t)la[i].n, la[i].y, la[i].bf16, s);
+  return e;
+}
+
+hipError_t launch_skinny(const LinearArgs& la, void* workspace, size_t workspace_bytes, hipStream_t s) {
+  return launch_skinny_multi(&la, 1, workspace, workspace_bytes, s);
 }
 
 }  // namespace mq

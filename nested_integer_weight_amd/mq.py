@@ -186,24 +186,25 @@ def linear_mixed(calls: list, workspace: Workspace | None = _default_ws) -> list
     dev = calls[0].x.device
     arr = (_lib.MqCall * len(calls))()
     outs = []
-    ws_need = 0
+    structs = []
     for i, c in enumerate(calls):
         _check_layer_args(c.x, c.packed, c.scales, c.zeros, c.group)
         m = c.x.shape[0]
         y = c.out if c.out is not None else torch.empty((m, c.packed.n), dtype=c.x.dtype, device=dev)
         outs.append(y)
-        ws_need = max(ws_need, workspace_bytes(m, c.packed.n, c.packed.k))
+        structs.append(c.packed.cstruct())
         e = arr[i]
         e.x = c.x.data_ptr()
         e.x_dtype = _DTYPES[c.x.dtype]
         e.m = m
-        e.w = ctypes.pointer(c.packed.cstruct())
+        e.w = ctypes.pointer(structs[-1])
         e.r = c.r
         e.rule = RULES[c.rule]
         e.group = c.group
         e.scales = c.scales.data_ptr()
         e.zeros = c.zeros.data_ptr()
         e.y = y.data_ptr()
+    ws_need = int(_lib.lib().mq_linear_mixed_workspace_bytes(arr, len(calls)))
     ws = workspace.get(ws_need, dev) if workspace is not None else None
     failed = ctypes.c_int32(-1)
     st = _lib.lib().mq_linear_mixed(arr, len(calls), _ptr(ws), 0 if ws is None else ws.numel(),

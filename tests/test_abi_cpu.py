@@ -173,3 +173,22 @@ def _produce(L, w=4096, n=64, k=256, group=64, widths=(3, 4, 8), lams=(1.0, 1.0,
 ])
 def test_produce_validation(L, kw, status):
     assert _produce(L, **kw) == status
+
+
+def test_mixed_workspace_query_is_pure(L):
+    w1 = _packed(n=14336, k=4096)
+    w2 = _packed(n=4096, k=14336)
+    arr = (_lib.MqCall * 3)()
+    for i, w in enumerate((w1, w1, w2)):
+        arr[i].x, arr[i].x_dtype, arr[i].m, arr[i].w = 4096, 1, 8, ctypes.pointer(w)
+        arr[i].r, arr[i].rule, arr[i].group = 2, 0, 128
+        arr[i].scales, arr[i].zeros, arr[i].y = 8192, 12288, 16384 + 4096 * i
+    single = max(L.mq_linear_workspace_bytes(8, w.n, w.k) for w in (w1, w1, w2))
+    got = L.mq_linear_mixed_workspace_bytes(arr, 3)
+    assert got >= single and got % 4 == 0
+    assert L.mq_linear_mixed_workspace_bytes(arr, 3) == got           # pure: same answer again
+    assert L.mq_linear_mixed_workspace_bytes(None, 3) == 0
+    assert L.mq_linear_mixed_workspace_bytes(arr, 0) == 0
+    for i in range(3):
+        arr[i].m = 1                                                     # GEMV calls: no workspace
+    assert L.mq_linear_mixed_workspace_bytes(arr, 3) == 0

@@ -309,6 +309,40 @@ def test_mixed_heterogeneous_gemv_launch(mq, r, rule, dt):
         check_y(y, lay, lay.x, c.r, c.rule)
 
 
+@pytest.mark.parametrize("m,dt,r,rule", [(8, "f16", 2, O.PREFIX), (16, "bf16", 3, O.ROUND), (40, "f16", 8, O.PREFIX),
+                                         (64, "bf16", 4, O.PREFIX), (5, "f16", 6, O.ROUND)])
+@pytest.mark.parametrize("ws", ["full", "one_split", "none"])
+def test_mixed_skinny_calls_share_launches(mq, m, dt, r, rule, ws):
+    """Independent skinny calls (gate/up-like wide calls that do not split k,
+    down-like narrow calls that do) share launches; with a workspace for every
+    split, for only one, or none, each result equals its single call with the
+    same workspace bit for bit, and the oracle within tolerance."""
+    specs = [(1536, 1024), (1536, 1024), (256, 3072), (320, 2048), (256, 3072), (64, 256)]
+    calls, lays = [], []
+    for i, (n, k) in enumerate(specs):
+        lay = synth.make_layer(cfg_id=11, tensor_id=10 * i + r, n=n, k=k, m=m, group=128, x_dtype=dt)
+        q, s, z = to_dev(lay)
+        calls.append(mq.Call(x=lay.x.to(DEV), packed=mq.pack_parent(q).truncated(r, rule), r=r, rule=rule,
+                             group=128, scales=s, zeros=z))
+        lays.append(lay)
+    single_need = max(mq.workspace_bytes(m, c.packed.n, c.packed.k) for c in calls)
+    if ws == "full":
+        wsp = mq.Workspace()
+    elif ws == "one_split":
+        wsp = mq.Workspace()
+        wsp.get(single_need, torch.device(DEV))
+        wsp.get = (lambda f: (lambda nbytes, dev: f(min(nbytes, single_need), dev)))(wsp.get)
+    else:
+        wsp = None
+    print(f"[skinny-mixed] m={m} dt={dt} r={r} rule={rule} ws={ws}", flush=True)
+    outs = mq.linear_mixed(calls, workspace=wsp)
+    for c, lay, y in zip(calls, lays, outs):
+        single = mq.linear(c.x, c.packed, c.r, c.rule, c.group, c.scales, c.zeros,
+                           workspace=None if ws == "none" else mq.Workspace())
+        assert torch.equal(single, y)
+        check_y(y, lay, lay.x, c.r, c.rule)
+
+
 def test_mixed_hazards_beyond_activations(mq):
     # a call whose output is another call's scale array must run before that
     # call reads it, and after an earlier call that reads the old scales
