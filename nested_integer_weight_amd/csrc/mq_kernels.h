@@ -51,7 +51,7 @@ __host__ inline bool skinny_eligible(int m, int k, int rule) { return skinny_sha
 struct SkinnyPlan {
   int splits;            // k ranges (1 = no workspace)
   int rounds_per_split;  // 256-wide k rounds per range
-  int nt;                // 16-row tiles per wave: 1 (64-row workgroups) or 2 (128-row)
+  int nt;                // 16-row tiles per wave: 1 (64-row workgroups; the only plan taken)
   int kh;                // teams of 4 waves per workgroup splitting its k range (1 or 2)
   int run;               // 64-code runs per lane, row and round (1 or 2)
 };
