@@ -195,10 +195,10 @@ mq_status mq_linear_noalloc(const void* x, int32_t x_dtype, int32_t m, const mq_
  * independent (no call writes memory that another call of the run reads or
  * writes: x, the planes its width needs, scales, zeros, y).  Runs execute in
  * order.  Inside a run, every call that takes the register GEMV (fp16 x with
- * m <= 4, bf16 x with m == 1, k <= 16384) with the same m, width, rule and
- * dtype joins one launch (up to 32 calls of any shape, e.g. the gate, up and
- * down projections of a decode step, or the projections of several
- * Mix'n'Match blocks); skinny-path calls (see mq_linear) with the same m,
+ * m <= 4, bf16 x with m == 1, k <= 16384) with the same m, rule and dtype
+ * joins one launch (up to 32 calls of any width and shape, e.g. the gate, up
+ * and down projections of a decode step, or the projections of several
+ * Mix'n'Match blocks at their own widths); skinny-path calls (see mq_linear) with the same m,
  * width, rule, dtype and planned workgroup shape join one launch too (up to
  * 8 calls), each keeping its own k split as long as the workspace holds all
  * of them (mq_linear_mixed_workspace_bytes); the other calls run one by one.

@@ -132,10 +132,10 @@ bool writes_into(const mq_call& c, const mq_call& d) {
 // results in any order or at the same time.
 bool independent(const mq_call& c, const mq_call& d) { return !writes_into(c, d) && !writes_into(d, c); }
 
-// The launch class of a GEMV-eligible call: calls of one class can share a
-// GEMV launch.
+// The launch class of a GEMV-eligible call: calls of one class (any width
+// and shape) can share a GEMV launch.
 bool same_gemv_class(const mq_call& c, const mq_call& d) {
-  return c.m == d.m && c.r == d.r && c.rule == d.rule && c.x_dtype == d.x_dtype;
+  return c.m == d.m && c.rule == d.rule && c.x_dtype == d.x_dtype;
 }
 bool gemv_call(const mq_call& c) { return c.m > 0 && gemv_eligible(c.m, c.w->k, c.x_dtype == MQ_BF16); }
 bool skinny_call(const mq_call& c) { return c.m > 0 && !gemv_call(c) && skinny_eligible(c.m, c.w->k, c.rule); }
@@ -308,8 +308,8 @@ mq_status mq_linear_mixed(const mq_call* calls, int32_t n_calls, void* workspace
     }
   }
   // Runs of consecutive, pairwise independent calls: inside a run the order
-  // does not matter, so every GEMV-eligible call of one class (m, width,
-  // rule, dtype) goes into one launch, whatever its shape, skinny calls of
+  // does not matter, so every GEMV-eligible call of one class (m, rule,
+  // dtype) goes into one launch, whatever its width and shape, skinny calls of
   // one launch shape share launches, and the other calls run one by one.
   // Runs follow each other in stream order.
   for (int32_t i = 0; i < n_calls;) {

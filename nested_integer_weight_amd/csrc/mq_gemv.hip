@@ -12,9 +12,10 @@
 //    lane owning a fixed 64-code k-slice of the group's rows, so its slice of
 //    X sits in VGPRs for every row it walks.  One 256-thread workgroup per
 //    item; a launch covers the items of up to kGemvMaxCalls calls of one
-//    width, rule, m and dtype (any n, k and group), found by a scalar search
-//    of the kernel arguments.  Independent calls (gate, up and down of an FFN
-//    at one width, or a whole Mix'n'Match pass) then share one launch ramp
+//    rule, m and dtype (any width, n, k and group), found by a scalar search
+//    of the kernel arguments; the call's width selects the code path of the
+//    workgroup.  Independent calls (gate, up and down of an FFN, a whole
+//    Mix'n'Match pass at its per-layer widths) then share one launch ramp
 //    and drain.
 //  * Loads.  Buffer loads: the row group's first row is the base of a
 //    descriptor in scalar registers, the row a scalar offset and the lane's
@@ -56,6 +57,7 @@ struct GemvCall {
   const uint16_t* s;
   const uint16_t* z;
   int n, k;
+  int r;      // width (the kernel branches on it per workgroup)
   int item0;  // first item of the call
   int wlog;   // log2 of the waves sharing a row (W = 1, 2 or 4)
   int rpi;    // rows per item: (4 / W) row groups x ROWS
@@ -421,14 +423,8 @@ struct GemvWave {
 // activations of its call with the other three waves through LDS; wider rows
 // split the slices over 2 or 4 waves and each lane loads its own.
 template <int R, int RULE, int MT, int BF16, int ROWS>
-__global__ __launch_bounds__(256) void gemv_multi_kernel(GemvLaunch a) {
+__device__ __forceinline__ void gemv_item(const GemvLaunch& a, const GemvCall& C, int it, float* red, uint4* xlds) {
   using Wave = GemvWave<R, RULE, MT, BF16, ROWS>;
-  __shared__ float red[4 * Wave::V];
-  __shared__ uint4 xlds[MT * 8 * 64];  // [token][piece][slice] for one-wave rows
-  const int it = (int)blockIdx.x;
-  int c = 0;
-  while (c + 1 < a.ncalls && it >= a.c[c + 1].item0) ++c;
-  const GemvCall& C = a.c[c];
   const int wave = uniform((int)(threadIdx.x >> 6));
   const int lane = (int)(threadIdx.x & 63);
   Wave w(C, it, wave, lane);
@@ -480,9 +476,29 @@ __global__ __launch_bounds__(256) void gemv_multi_kernel(GemvLaunch a) {
   w.finish(red, a.m);
 }
 
+// One workgroup per item: the item's call is found by a scalar search of the
+// kernel arguments, and its width picks the code path (uniform over the
+// workgroup), so one launch can hold calls of every width.
+template <int RULE, int MT, int BF16, int ROWS>
+__global__ __launch_bounds__(256) void gemv_multi_kernel(GemvLaunch a) {
+  __shared__ float red[4 * ROWS * MT];
+  __shared__ uint4 xlds[MT * 8 * 64];  // [token][piece][slice] for one-wave rows
+  const int it = (int)blockIdx.x;
+  int c = 0;
+  while (c + 1 < a.ncalls && it >= a.c[c + 1].item0) ++c;
+  const GemvCall& C = a.c[c];
+  switch (C.r) {
+    case 2: gemv_item<2, RULE, MT, BF16, ROWS>(a, C, it, red, xlds); break;
+    case 3: gemv_item<3, RULE, MT, BF16, ROWS>(a, C, it, red, xlds); break;
+    case 4: gemv_item<4, RULE, MT, BF16, ROWS>(a, C, it, red, xlds); break;
+    case 6: gemv_item<6, RULE, MT, BF16, ROWS>(a, C, it, red, xlds); break;
+    default: gemv_item<8, RULE, MT, BF16, ROWS>(a, C, it, red, xlds); break;
+  }
+}
+
 int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 
-template <int R, int RULE, int MT, int BF16>
+template <int RULE, int MT, int BF16>
 hipError_t gemv_launch_t(const LinearArgs* la, int ncalls, hipStream_t s) {
   constexpr int ROWS = gemv_rows(MT);
   GemvLaunch a;
@@ -496,6 +512,7 @@ hipError_t gemv_launch_t(const LinearArgs* la, int ncalls, hipStream_t s) {
     c.z = la[i].zeros;
     c.n = la[i].n;
     c.k = la[i].k;
+    c.r = la[i].r;
     c.item0 = items;
     const int W = waves_per_row(la[i].k);
     c.wlog = W == 1 ? 0 : W == 2 ? 1 : 2;
@@ -509,46 +526,41 @@ hipError_t gemv_launch_t(const LinearArgs* la, int ncalls, hipStream_t s) {
   for (int i = ncalls; i < kGemvMaxCalls; ++i) a.c[i] = a.c[ncalls - 1];
   a.ncalls = ncalls;
   a.m = la[0].m;
-  hipLaunchKernelGGL((gemv_multi_kernel<R, RULE, MT, BF16, ROWS>), dim3((unsigned)items), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((gemv_multi_kernel<RULE, MT, BF16, ROWS>), dim3((unsigned)items), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-template <int R, int RULE, int BF16>
+template <int RULE, int BF16>
 hipError_t gemv_launch_m(const LinearArgs* a, int n, hipStream_t s) {
   if constexpr (BF16) {
-    return gemv_launch_t<R, RULE, 1, 1>(a, n, s);  // bf16: m == 1 only
+    return gemv_launch_t<RULE, 1, 1>(a, n, s);  // bf16: m == 1 only
   } else {
     switch (a[0].m) {
-      case 1: return gemv_launch_t<R, RULE, 1, 0>(a, n, s);
-      case 2: return gemv_launch_t<R, RULE, 2, 0>(a, n, s);
-      default: return gemv_launch_t<R, RULE, 4, 0>(a, n, s);
+      case 1: return gemv_launch_t<RULE, 1, 0>(a, n, s);
+      case 2: return gemv_launch_t<RULE, 2, 0>(a, n, s);
+      default: return gemv_launch_t<RULE, 4, 0>(a, n, s);
     }
   }
 }
 
-template <int R, int RULE>
+template <int RULE>
 hipError_t gemv_launch_d(const LinearArgs* a, int n, hipStream_t s) {
-  return a[0].bf16 ? gemv_launch_m<R, RULE, 1>(a, n, s) : gemv_launch_m<R, RULE, 0>(a, n, s);
+  return a[0].bf16 ? gemv_launch_m<RULE, 1>(a, n, s) : gemv_launch_m<RULE, 0>(a, n, s);
 }
 
 }  // namespace
 
 hipError_t launch_gemv_multi(const LinearArgs* a, int ncalls, hipStream_t s) {
   if (ncalls < 1 || ncalls > kGemvMaxCalls) return hipErrorInvalidValue;
-#define MQ_GEMV_CASE(RR)                                                               \
-  case RR:                                                                             \
-    return a[0].rule == kRuleExtra ? gemv_launch_d<RR, kRuleExtra>(a, ncalls, s)     \
-           : a[0].rule == kRuleRound ? gemv_launch_d<RR, kRuleRound>(a, ncalls, s)          \
-                                    : gemv_launch_d<RR, kRulePrefix>(a, ncalls, s);
-  switch (a[0].r) {
-    MQ_GEMV_CASE(2)
-    MQ_GEMV_CASE(3)
-    MQ_GEMV_CASE(4)
-    MQ_GEMV_CASE(6)
-    MQ_GEMV_CASE(8)
-    default: return hipErrorInvalidValue;
+  for (int i = 0; i < ncalls; ++i) {
+    const int r = a[i].r;
+    if ((r != 2 && r != 3 && r != 4 && r != 6 && r != 8) || a[i].rule != a[0].rule || a[i].m != a[0].m ||
+        a[i].bf16 != a[0].bf16)
+      return hipErrorInvalidValue;
   }
-#undef MQ_GEMV_CASE
+  return a[0].rule == kRuleExtra   ? gemv_launch_d<kRuleExtra>(a, ncalls, s)
+         : a[0].rule == kRuleRound ? gemv_launch_d<kRuleRound>(a, ncalls, s)
+                                   : gemv_launch_d<kRulePrefix>(a, ncalls, s);
 }
 
 }  // namespace mq

@@ -36,8 +36,8 @@ constexpr int kGemvMaxK = 16384;
 __host__ inline bool gemv_eligible(int m, int k, int bf16) {
   return m >= 1 && k <= kGemvMaxK && (bf16 ? m == 1 : m <= kGemvMaxM);
 }
-// Up to kGemvMaxCalls independent GEMV-eligible calls that share m, width,
-// rule and dtype (any n, k, group) in one launch.  No call may write what
+// Up to kGemvMaxCalls independent GEMV-eligible calls that share m, rule and
+// dtype (any width, n, k, group) in one launch.  No call may write what
 // another call of the launch reads or writes.
 constexpr int kGemvMaxCalls = 32;
 hipError_t launch_gemv_multi(const LinearArgs* a, int ncalls, hipStream_t s);

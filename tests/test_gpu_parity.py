@@ -343,6 +343,29 @@ def test_mixed_skinny_calls_share_launches(mq, m, dt, r, rule, ws):
         check_y(y, lay, lay.x, c.r, c.rule)
 
 
+@pytest.mark.parametrize("m,dt,rule", [(1, "f16", O.PREFIX), (2, "f16", O.ROUND), (4, "f16", O.EXTRA),
+                                       (1, "bf16", O.PREFIX), (3, "f16", O.PREFIX)])
+def test_mixed_all_widths_one_gemv_launch(mq, m, dt, rule):
+    """Calls at every width (and several shapes) of one GEMV class share one
+    launch, each workgroup taking its call's width: every result equals its
+    single call bit for bit and the oracle within tolerance."""
+    specs = [(2, 300, 4096), (3, 77, 14336), (4, 130, 6144), (6, 64, 1024), (8, 200, 4096), (2, 33, 8192),
+             (8, 48, 14336), (4, 16, 512)]
+    calls, lays = [], []
+    for i, (r, n, k) in enumerate(specs):
+        lay = synth.make_layer(cfg_id=12, tensor_id=10 * i + m, n=n, k=k, m=m, group=128, x_dtype=dt)
+        q, s_, z = to_dev(lay)
+        calls.append(mq.Call(x=lay.x.to(DEV), packed=mq.pack_parent(q).truncated(r, rule), r=r, rule=rule,
+                             group=128, scales=s_, zeros=z))
+        lays.append(lay)
+    print(f"[all-widths] m={m} dt={dt} rule={rule}", flush=True)
+    outs = mq.linear_mixed(calls)
+    for c, lay, y in zip(calls, lays, outs):
+        single = mq.linear(c.x, c.packed, c.r, c.rule, c.group, c.scales, c.zeros)
+        assert torch.equal(single, y)
+        check_y(y, lay, lay.x, c.r, c.rule)
+
+
 def test_mixed_hazards_beyond_activations(mq):
     # a call whose output is another call's scale array must run before that
     # call reads it, and after an earlier call that reads the old scales
