@@ -102,12 +102,34 @@ __global__ __launch_bounds__(kSearchThreads) void scale_search_kernel(
     if ((sb & 0x7FFFu) == 0) sb = 0x3C00u;  // 1.0
     const float s = h2f(sb);
     const float z = fminf(fmaxf(rintf(-lo_p / s), 0.0f), 255.0f) + 0.0f;  // +0, never -0
+    // The nearest code needs rint of the correctly rounded w / s.  With the
+    // reciprocal r = RN(1 / s), y = RN(w r) is within 4 units in the last
+    // place of RN(w / s) (two roundings of 2^-24 each, plus the quotient's
+    // own), so rint(y) is the same integer unless a half-integer lies within
+    // that distance of y; only then (about one weight in 4000) is the quotient
+    // divided out.  Beyond |y| = 600 both clamp to the same code (|z| <= 255).
+    const float rs = 1.0f / s;
+    // v_r(q) - z for the true prefix as float(q & mask) + (delta_r - z): exact
+    float cz[NR];
+#pragma unroll
+    for (int t = 0; t < NR; ++t) cz[t] = W.delta[t] - z;
     float acc = 0.0f;
     for (int j = 0; j < group; ++j) {
       const float wj = wg[j];
-      const int q = (int)fminf(fmaxf(rintf(wj / s) + z, 0.0f), 255.0f);
+      const float y = wj * rs;
+      const float ay = fabsf(y);
+      float qf = rintf(y);
+      if (fabsf((y - floorf(y)) - 0.5f) <= ay * 0x1p-21f && ay <= 600.0f) qf = rintf(wj / s);
+      const int q = (int)fminf(fmaxf(qf + z, 0.0f), 255.0f);
 #pragma unroll
-      for (int t = 0; t < NR; ++t) acc = acc + weighted_term(wj, s, z, slice_value<RULE>(q, W, t), W.lam[t]);
+      for (int t = 0; t < NR; ++t) {
+        float vz;  // v_r(q) - z, exact
+        if constexpr (RULE == kRulePrefix) vz = (float)(q & W.mask[t]) + cz[t];
+        else vz = slice_value<RULE>(q, W, t) - z;
+        const float d = wj - s * vz;
+        const float dd = d * d;
+        acc = acc + W.lam[t] * dd;
+      }
     }
     err[gb * n_grid + i] = acc;
   }
