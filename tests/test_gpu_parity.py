@@ -453,6 +453,29 @@ def test_llama_ffn_decode_m1(mq, llama_ffn, r):
         check_y(y, lay, x, r, O.PREFIX, w64=w64_of(tid, lay, r, O.PREFIX))
 
 
+def test_llama_ffn_decode_step_one_launch(mq, llama_ffn):
+    """The decode step of the benchmark: gate, up and down at r = 2, 3, 4, 6
+    and 8 (15 calls) in one mq_linear_mixed call, i.e. one launch; every
+    output equals its single call bit for bit (single calls are checked
+    against the oracle at these shapes above), and the r = 2 and r = 8
+    outputs also against the oracle directly."""
+    calls, singles = [], []
+    for r in WIDTHS:
+        for tid, lay, pk, s, z in llama_ffn:
+            x = synth.activations(synth.rng_for(2, 10 + r), 1, lay.k, "f16").to(DEV)
+            calls.append(mq.Call(x=x, packed=pk.truncated(r), r=r, rule=O.PREFIX, group=128, scales=s, zeros=z))
+            singles.append(mq.linear(x, pk.truncated(r), r, O.PREFIX, 128, s, z))
+    outs = mq.linear_mixed(calls)
+    for c, y, y1 in zip(calls, outs, singles):
+        assert torch.equal(y, y1), (c.r, c.packed.n, c.packed.k)
+    i = 0
+    for r in WIDTHS:
+        for tid, lay, pk, s, z in llama_ffn:
+            if r in (2, 8):
+                check_y(outs[i], lay, calls[i].x.cpu(), r, O.PREFIX, w64=w64_of(tid, lay, r, O.PREFIX))
+            i += 1
+
+
 @pytest.mark.parametrize("r", [2, 3, 4, 8])
 def test_llama_ffn_skinny(mq, llama_ffn, r):
     for tid, lay, pk, s, z in llama_ffn:
@@ -556,12 +579,14 @@ def test_gemma_mixnmatch_blocks(mq, m, dt):
 
 
 def test_graph_replay_matches_eager(mq):
-    # the serving form: calls captured in a HIP graph (GEMV, skinny with split-k,
-    # GEMM with split-k) replay bit for bit like the eager calls, replay after
-    # replay, with eager work and synchronisation in between
+    # the serving form: calls captured in a HIP graph (GEMV calls of two widths
+    # sharing a launch, skinny calls with split-k sharing a launch, a skinny
+    # bf16 call, GEMM with split-k) replay bit for bit like the eager calls,
+    # replay after replay, with eager work and synchronisation in between
     calls = []
     for i, (r, m, dt, n, k) in enumerate([(2, 1, "f16", 512, 4096), (4, 16, "f16", 640, 4096),
-                                          (8, 40, "bf16", 384, 2048), (3, 300, "bf16", 520, 1024)]):
+                                          (8, 40, "bf16", 384, 2048), (3, 300, "bf16", 520, 1024),
+                                          (8, 1, "f16", 256, 1024), (4, 16, "f16", 320, 2048)]):
         lay = synth.make_layer(cfg_id=7, tensor_id=i, n=n, k=k, m=m, group=128, x_dtype=dt)
         q, s, z = to_dev(lay)
         x = lay.x.to(DEV)
