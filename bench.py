@@ -15,8 +15,8 @@ per pass through it (four times the 256 MB MALL): weight reads come from HBM,
 not the last-level cache.
 
 Timing (one declared mode): the calls are captured in HIP graphs (checked bit
-for bit against eager calls first) and replayed; HIP events on the launch
-stream bracket the replays.
+for bit against eager calls first) and replayed, five decode steps per graph;
+HIP events on the launch stream bracket the replays.
   value        algorithmic bytes of all calls of the timed steps / their time
                (GB/s).  Algorithmic bytes per call = bit planes the width reads
                + 4 B (fp16 scale + zero) per group + X (2*M*K) + Y (2*M*N).
@@ -64,6 +64,7 @@ PREFILL_WIDTHS = (2, 4, 8)
 GROUP = 128
 RING_BYTES = 1 << 30           # bytes each timed piece reads per pass through the ring
 MIN_LAUNCHES = 200             # launches averaged per per-launch figure
+GRAPH_STEPS = 5                # decode steps per graph in the timed region
 METRIC = "sliced W·X: decode GB/s (packed bytes, %HBM peak) + prefill TFLOP/s (%MFMA) per r"
 PLANE_BITS = (2, 1, 1, 2, 2)
 PLANES_FOR_R = {2: 1, 3: 2, 4: 3, 6: 4, 8: 5}
@@ -209,28 +210,28 @@ def main():
         return True
 
     # ---------------- timed steps: HIP graph replay ----------------
-    # One graph holds `gsteps` consecutive steps of the ring; the timed region
-    # replays it, plus one graph of the leftover steps, so exactly --steps
-    # steps are timed and consecutive steps read different parent copies.
-    gsteps = min(args.steps, ring)
-    g_step = capture(lambda: [step_calls(i) for i in range(gsteps)])
-    if not check_replay(g_step, lambda: [step_calls(i) for i in range(gsteps)]):
-        raise RuntimeError("graph replay of the decode step differs from the eager calls")
-    rem = args.steps % gsteps
-    g_rem = capture(lambda: [step_calls(i) for i in range(rem)]) if rem else None
+    # Graphs of GRAPH_STEPS consecutive steps each (one launch per step),
+    # covering the timed steps in order, so exactly --steps steps are timed and
+    # consecutive steps read different parent copies.  While the GPU runs one
+    # graph the host submits the next; after the synchronisation that opens
+    # the timed region the GPU waits only for the first (short) submission.
+    segs = [(a, min(a + GRAPH_STEPS, args.steps)) for a in range(0, args.steps, GRAPH_STEPS)]
+    step_graphs = [capture(lambda a=a, b=b: [step_calls(i) for i in range(a, b)]) for a, b in segs]
+    for gi in sorted({0, len(segs) - 1}):
+        a, b = segs[gi]
+        if not check_replay(step_graphs[gi], lambda a=a, b=b: [step_calls(i) for i in range(a, b)]):
+            raise RuntimeError("graph replay of the decode step differs from the eager calls")
     torch.cuda.synchronize()
     t0_, t1_ = ev(), ev()
     t0_.record(stream)
-    for _ in range(args.steps // gsteps):
-        g_step.replay()
-    if g_rem is not None:
-        g_rem.replay()
+    for g in step_graphs:
+        g.replay()
     t1_.record(stream)
     torch.cuda.synchronize()
     step_ms = t0_.elapsed_time(t1_) / args.steps
     value = bytes_step / (step_ms * 1e-3) / 1e9
     log(f"[bench] {args.steps} steps (graph replay): {step_ms * 1e3:.1f} us/step, {value:.1f} GB/s")
-    del g_step, g_rem
+    del step_graphs
 
     # secondary: the same steps issued as eager C-ABI calls (host gaps included)
     torch.cuda.synchronize()
