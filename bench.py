@@ -243,6 +243,21 @@ def main():
     eager_ms = t0_.elapsed_time(t1_) / args.steps
     eager = {"value": round(bytes_step / (eager_ms * 1e-3) / 1e9, 1), "ms_per_step": round(eager_ms, 5)}
     log(f"[bench] eager: {eager_ms * 1e3:.1f} us/step")
+    # and with the call lists checked and marshalled once (mq.PreparedCalls):
+    # one C-ABI call per step, the host cost of a serving loop without graphs
+    prepared = [mq.PreparedCalls([c for r in WIDTHS for c in calls_for(i, r)]) for i in range(min(args.steps, ring))]
+    prepared[0].run()
+    torch.cuda.synchronize()
+    t0_.record(stream)
+    for i in range(args.steps):
+        prepared[i % len(prepared)].run()
+    t1_.record(stream)
+    torch.cuda.synchronize()
+    prep_ms = t0_.elapsed_time(t1_) / args.steps
+    eager["prepared_ms_per_step"] = round(prep_ms, 5)
+    eager["prepared_value"] = round(bytes_step / (prep_ms * 1e-3) / 1e9, 1)
+    log(f"[bench] eager, prepared call lists: {prep_ms * 1e3:.1f} us/step")
+    del prepared
 
     # ---------------- per-launch figures ----------------
     # The fused launch of each width (gate, up and down), and for comparison the

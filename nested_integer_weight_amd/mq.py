@@ -179,39 +179,57 @@ class Call:
     out: torch.Tensor | None = None
 
 
+class PreparedCalls:
+    """A fixed list of calls checked and marshalled into the C-ABI call array
+    once; run() issues them with one mq_linear_mixed call.  For serving loops
+    that repeat the same calls on the same buffers: the tensors (inputs,
+    planes, scales, zero points, outputs) must stay alive and keep their
+    storage; their contents may change between runs."""
+
+    def __init__(self, calls: list, workspace: Workspace | None = _default_ws):
+        self.n = len(calls)
+        self.outs = []
+        self._workspace = workspace
+        if not calls:
+            return
+        self.dev = calls[0].x.device
+        self._arr = (_lib.MqCall * len(calls))()
+        self._keep = []
+        for i, c in enumerate(calls):
+            _check_layer_args(c.x, c.packed, c.scales, c.zeros, c.group)
+            m = c.x.shape[0]
+            y = c.out if c.out is not None else torch.empty((m, c.packed.n), dtype=c.x.dtype, device=self.dev)
+            _need_cuda(y, "out", c.x.dtype)
+            self.outs.append(y)
+            self._keep.append((c.x, c.scales, c.zeros, y, c.packed))
+            e = self._arr[i]
+            e.x = c.x.data_ptr()
+            e.x_dtype = _DTYPES[c.x.dtype]
+            e.m = m
+            e.w = ctypes.pointer(c.packed.cstruct())
+            e.r = c.r
+            e.rule = RULES[c.rule]
+            e.group = c.group
+            e.scales = c.scales.data_ptr()
+            e.zeros = c.zeros.data_ptr()
+            e.y = y.data_ptr()
+        self._ws_need = int(_lib.lib().mq_linear_mixed_workspace_bytes(self._arr, self.n))
+        self._failed = ctypes.c_int32(-1)
+
+    def run(self) -> list:
+        if not self.n:
+            return []
+        ws = self._workspace.get(self._ws_need, self.dev) if self._workspace is not None else None
+        st = _lib.lib().mq_linear_mixed(self._arr, self.n, _ptr(ws), 0 if ws is None else ws.numel(),
+                                        ctypes.byref(self._failed), _stream(self.dev))
+        if st != 0:
+            raise MqError(st, f"mq_linear_mixed (call {self._failed.value})")
+        return self.outs
+
+
 def linear_mixed(calls: list, workspace: Workspace | None = _default_ws) -> list:
     """Mix'n'Match: each call at its own width, in order on the current stream."""
-    if not calls:
-        return []
-    dev = calls[0].x.device
-    arr = (_lib.MqCall * len(calls))()
-    outs = []
-    structs = []
-    for i, c in enumerate(calls):
-        _check_layer_args(c.x, c.packed, c.scales, c.zeros, c.group)
-        m = c.x.shape[0]
-        y = c.out if c.out is not None else torch.empty((m, c.packed.n), dtype=c.x.dtype, device=dev)
-        outs.append(y)
-        structs.append(c.packed.cstruct())
-        e = arr[i]
-        e.x = c.x.data_ptr()
-        e.x_dtype = _DTYPES[c.x.dtype]
-        e.m = m
-        e.w = ctypes.pointer(structs[-1])
-        e.r = c.r
-        e.rule = RULES[c.rule]
-        e.group = c.group
-        e.scales = c.scales.data_ptr()
-        e.zeros = c.zeros.data_ptr()
-        e.y = y.data_ptr()
-    ws_need = int(_lib.lib().mq_linear_mixed_workspace_bytes(arr, len(calls)))
-    ws = workspace.get(ws_need, dev) if workspace is not None else None
-    failed = ctypes.c_int32(-1)
-    st = _lib.lib().mq_linear_mixed(arr, len(calls), _ptr(ws), 0 if ws is None else ws.numel(),
-                                    ctypes.byref(failed), _stream(dev))
-    if st != 0:
-        raise MqError(st, f"mq_linear_mixed (call {failed.value})")
-    return outs
+    return PreparedCalls(calls, workspace).run()
 
 
 def slice_codes(packed: Packed, r: int, rule) -> torch.Tensor:

@@ -366,6 +366,27 @@ def test_mixed_all_widths_one_gemv_launch(mq, m, dt, rule):
         check_y(y, lay, lay.x, c.r, c.rule)
 
 
+def test_prepared_calls_rerun_with_new_inputs(mq):
+    """mq.PreparedCalls marshals a call list once; rerunning it after the
+    inputs changed in place gives what a fresh mq_linear_mixed call gives."""
+    specs = [(2, 1, "f16", 300, 4096), (8, 1, "f16", 200, 1024), (4, 16, "f16", 320, 2048), (3, 300, "bf16", 256, 1024)]
+    calls = []
+    for i, (r, m, dt, n, k) in enumerate(specs):
+        lay = synth.make_layer(cfg_id=13, tensor_id=i, n=n, k=k, m=m, group=128, x_dtype=dt)
+        q, s_, z = to_dev(lay)
+        calls.append(mq.Call(x=lay.x.to(DEV), packed=mq.pack_parent(q), r=r, rule=O.PREFIX, group=128,
+                             scales=s_, zeros=z))
+    prep = mq.PreparedCalls(calls)
+    for rep in range(2):
+        outs = [y.clone() for y in prep.run()]
+        ref = mq.linear_mixed([mq.Call(x=c.x, packed=c.packed, r=c.r, rule=c.rule, group=c.group, scales=c.scales,
+                                       zeros=c.zeros) for c in calls])
+        for a, b in zip(outs, ref):
+            assert torch.equal(a, b), rep
+        for c in calls:
+            c.x.mul_(-0.5)  # new inputs, same storage
+
+
 def test_mixed_hazards_beyond_activations(mq):
     # a call whose output is another call's scale array must run before that
     # call reads it, and after an earlier call that reads the old scales
