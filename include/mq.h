@@ -255,7 +255,7 @@ mq_status mq_dequant(const mq_packed* w, int32_t r, int32_t rule, int32_t group,
  * index order, widths innermost).  The pages store the error matrix in fp32.
  *
  * Shape rules as for the layer, plus group <= 1024 (MQ_ESHAPE) and n * k <=
- * 2^40 (MQ_ESIZE).  MQ_EINVAL for
+ * 2^36 (MQ_ESIZE).  MQ_EINVAL for
  * a bad n_widths, lambda, n_grid or grid_den; MQ_EWIDTH for a width outside
  * {2,3,4,6,8} or repeated.  Two launches on `stream`; no workspace. */
 mq_status mq_produce_parent(const float* w, int32_t n, int32_t k, int32_t group, const int32_t* widths,

@@ -412,7 +412,7 @@ mq_status mq_produce_parent(const float* w, int32_t n, int32_t k, int32_t group,
   st = check_group(k, group);
   if (st != MQ_OK) return st;
   if (group > kMaxProduceGroup) return MQ_ESHAPE;
-  if ((uint64_t)n * (uint64_t)k > (1ull << 40)) return MQ_ESIZE;
+  if ((uint64_t)n * (uint64_t)k > (1ull << 36)) return MQ_ESIZE;  // keeps every grid below 2^31 workgroups
   if (!valid_rule(rule)) return MQ_ERULE;
   if (n_widths < 1 || n_widths > kMaxProduceWidths) return MQ_EINVAL;
   for (int i = 0; i < n_widths; ++i) {
