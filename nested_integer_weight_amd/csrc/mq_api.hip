@@ -24,6 +24,8 @@ static_assert(MQ_PREFIX == kRulePrefix && MQ_ROUND == kRuleRound && MQ_ROUND_EXT
 mq_status check_shape(int n, int k) {
   if (n <= 0 || k <= 0) return MQ_EINVAL;
   if (k % 64) return MQ_ESHAPE;
+  // 2^40 codes (a 1 TB parent) keeps every per-unit grid far below 2^31 workgroups
+  if ((uint64_t)n * (uint64_t)k > (1ull << 40)) return MQ_ESIZE;
   return MQ_OK;
 }
 

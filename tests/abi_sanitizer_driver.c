@@ -50,7 +50,8 @@ static void pure_queries(void) {
       for (int p = -1; p <= MQ_NPLANES; ++p) (void)mq_plane_bytes(big[i], big[j], p);
   EXPECT(mq_plane_bytes(14336, 4096, 0), 14336LL * 4096 / 4);
   EXPECT(mq_plane_bytes(14336, 4096, 1), 14336LL * 4096 / 8);
-  EXPECT(mq_plane_bytes(2147483647, 2147483584, 0), (long long)(2147483647ULL * 2147483584ULL / 4));
+  EXPECT(mq_plane_bytes(1 << 20, 1 << 20, 0), (long long)((1ULL << 40) / 4));  /* at the size limit */
+  EXPECT(mq_plane_bytes(2147483647, 2147483584, 0), 0);                        /* beyond it */
   for (int r = -1; r < 10; ++r)
     for (int rule = -1; rule < 4; ++rule) (void)mq_planes_needed(r, rule);
   EXPECT(mq_planes_needed(2, MQ_PREFIX), 1);
