@@ -387,6 +387,53 @@ def test_prepared_calls_rerun_with_new_inputs(mq):
             c.x.mul_(-0.5)  # new inputs, same storage
 
 
+def test_mixed_long_list_many_launches(mq):
+    """300 small independent calls (more than one 256-call window, several
+    GEMV and skinny launches per class, GEMM calls in between, two rules):
+    every output equals its single call bit for bit."""
+    rng = np.random.default_rng(14)
+    pool = []
+    for i in range(6):
+        lay = synth.make_layer(cfg_id=14, tensor_id=i, n=64 * (i + 1), k=256 * (1 + i % 3), m=0, group=128)
+        q, s_, z = to_dev(lay)
+        pool.append((lay.n, lay.k, mq.pack_parent(q), s_, z))
+    calls = []
+    for j in range(300):
+        n, k, pk, s_, z = pool[rng.integers(len(pool))]
+        m = int(rng.choice([1, 1, 2, 4, 8, 16, 80]))
+        dt = "bf16" if (m > 4 and rng.integers(2)) else "f16"
+        r = int(rng.choice([2, 3, 4, 6, 8]))
+        rule = O.PREFIX if rng.integers(3) else O.ROUND
+        x = synth.activations(synth.rng_for(14, 100 + j), m, k, dt).to(DEV)
+        calls.append(mq.Call(x=x, packed=pk, r=r, rule=rule, group=128, scales=s_, zeros=z))
+    print("[long-list] 300 calls", flush=True)
+    outs = mq.linear_mixed(calls)
+    for c, y in zip(calls, outs):
+        single = mq.linear(c.x, c.packed, c.r, c.rule, c.group, c.scales, c.zeros)
+        assert torch.equal(single, y), (c.r, c.rule, c.x.shape, c.packed.n)
+
+
+def test_two_streams_own_workspaces(mq):
+    """Calls issued on two streams at once, each stream with its own split-k
+    workspace (mq.Workspace keys buffers by stream), give the single-stream
+    results bit for bit."""
+    lays = [synth.make_layer(cfg_id=15, tensor_id=i, n=512, k=4096, m=24, group=128, x_dtype="f16") for i in range(2)]
+    dev = [to_dev(l) for l in lays]
+    packs = [mq.pack_parent(q) for q, _, _ in dev]
+    xs = [l.x.to(DEV) for l in lays]
+    ref = [mq.linear(xs[i], packs[i], 4, O.PREFIX, 128, dev[i][1], dev[i][2]) for i in range(2)]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [None, None]
+    for rep in range(3):
+        for i in range(2):
+            with torch.cuda.stream(streams[i]):
+                outs[i] = mq.linear(xs[i], packs[i], 4, O.PREFIX, 128, dev[i][1], dev[i][2])
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert torch.equal(outs[i], ref[i]), (rep, i)
+
+
 def test_mixed_hazards_beyond_activations(mq):
     # a call whose output is another call's scale array must run before that
     # call reads it, and after an earlier call that reads the old scales
