@@ -8,13 +8,16 @@
 // "Efficient and Accurate Inference over Nested Quantized Models", section
 // 4, third component).  On gfx950:
 //  * Work items.  Every call's output rows are cut into items of 4 / W row
-//    groups x ROWS rows; a row group is W waves (W = 1, 2 or 4 by k), each
-//    lane owning a fixed 64-code k-slice of the group's rows, so its slice of
-//    X sits in VGPRs for every row it walks.  One 256-thread workgroup per
-//    item; a launch covers the items of up to kGemvMaxCalls calls of one
-//    rule, m and dtype (any width, n, k and group), found by a scalar search
-//    of the kernel arguments; the call's width selects the code path of the
-//    workgroup.  Independent calls (gate, up and down of an FFN, a whole
+//    groups x sets x ROWS rows; a row group is W waves (W = 1, 2 or 4 by k),
+//    each lane owning a fixed 64-code k-slice of the group's rows, so its
+//    slice of X sits in VGPRs for every row it walks.  A row group walks its
+//    rows in sets of ROWS, one reduction per set; launches with many items
+//    take two sets per item, which halves the share of the activation set-up
+//    per row and still leaves several workgroups per CU.  One 256-thread
+//    workgroup per item; a launch covers the items of up to kGemvMaxCalls
+//    calls of one rule, m and dtype (any width, n, k and group), found by a
+//    scalar search of the kernel arguments; the call's width selects the
+//    code path of the workgroup.  Independent calls (gate, up and down of an FFN, a whole
 //    Mix'n'Match pass at its per-layer widths) then share one launch ramp
 //    and drain.
 //  * Loads.  Buffer loads: the row group's first row is the base of a
@@ -60,7 +63,8 @@ struct GemvCall {
   int r;      // width (the kernel branches on it per workgroup)
   int item0;  // first item of the call
   int wlog;   // log2 of the waves sharing a row (W = 1, 2 or 4)
-  int rpi;    // rows per item: (4 / W) row groups x ROWS
+  int sets;   // row sets of ROWS rows that a row group walks (1, 2 or 4)
+  int rpi;    // rows per item: (4 / W) row groups x sets x ROWS
   int gpr;    // quantization groups per row, k / group
   int gmul;   // slice -> group index: (slice * gmul) >> 16 == slice / (group / 64)
 };
@@ -175,7 +179,7 @@ struct GemvWave {
   // the row's 64-code slices.
   __device__ __forceinline__ GemvWave(const GemvCall& call, int it, int w, int l) : C(call), wave(w), lane(l) {
     wsl = wave & ((1 << C.wlog) - 1);
-    row0 = (it - C.item0) * C.rpi + (wave >> C.wlog) * ROWS;
+    row0 = (it - C.item0) * C.rpi + (wave >> C.wlog) * ROWS * C.sets;
     const int sl = (wsl << 6) + lane;
     valid = sl < (C.k >> 6);
     slice = valid ? sl : 0;
@@ -192,15 +196,16 @@ struct GemvWave {
     vgroup = ((slice * C.gmul) >> 16) * 2;
   }
 
-  // Issue the plane, scale and zero loads of batch b into buffer BUF.  Rows
-  // past n are clamped to n - 1 (their results are not stored).
+  // Issue the plane, scale and zero loads of batch b of row set `set` into
+  // buffer BUF.  Rows past n are clamped to n - 1 (their results are not
+  // stored).
   template <int BUF>
-  __device__ __forceinline__ void load_batch(int b) {
+  __device__ __forceinline__ void load_batch(int set, int b) {
     const int base = min(row0, C.n - 1);
     const int rb2 = C.k >> 2, rb1 = C.k >> 3;
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
-      const int r = min(row0 + b * RB + i, C.n - 1) - base;  // uniform
+      const int r = min(row0 + set * ROWS + b * RB + i, C.n - 1) - base;  // uniform
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
         if (kPlaneBits[p] == 2) {
@@ -223,15 +228,15 @@ struct GemvWave {
   // Activations of this lane's slice in register form: fp16 pairs (natural
   // k order, or the field order of the width-2 fast path) or fp32 for bf16,
   // the slice's sum of X and, for the fast path, the sum of X times the fp16
-  // field offsets.  w[mm] holds the slice's 64 halves of token mm.
-  __device__ __forceinline__ void x_setup(const uint32_t (&w0)[MT][32], int m) {
+  // field offsets.  w0[mm] holds the slice's 64 halves of token mm.  Lanes
+  // past the row's last slice and tokens past m hold copies of real
+  // activations; what they compute is dropped (the per-row select of
+  // compute_batch, the token check of the store), so nothing is masked here.
+  __device__ __forceinline__ void x_setup(const uint32_t (&w0)[MT][32]) {
     constexpr uint32_t kOnes = 0x3C003C00u;  // (1.0, 1.0) in fp16
 #pragma unroll
     for (int mm = 0; mm < MT; ++mm) {
-      const uint32_t keep = (valid && mm < m) ? 0xFFFFFFFFu : 0u;
-      uint32_t w[32];
-#pragma unroll
-      for (int i = 0; i < 32; ++i) w[i] = w0[mm][i] & keep;
+      const uint32_t (&w)[32] = w0[mm];
       if constexpr (BF16) {
         float sum = 0.f;
 #pragma unroll
@@ -369,27 +374,32 @@ struct GemvWave {
     }
   }
 
-  // the first PD batches
   template <int B>
-  __device__ __forceinline__ void issue() {
+  __device__ __forceinline__ void issue(int set) {
     if constexpr (B < PD) {
-      load_batch<B>(B);
-      issue<B + 1>();
+      load_batch<B>(set, B);
+      issue<B + 1>(set);
     }
   }
-  // batch B computes from buffer B % PD, which then takes batch B + PD
+  // Batch B of row set `set` computes from buffer B % PD, which then takes
+  // the batch PD later: in this set, or the first ones of the next set (NB is
+  // a multiple of PD, so every set uses the buffers in the same order).
   template <int B>
-  __device__ __forceinline__ void run() {
+  __device__ __forceinline__ void run(int set) {
     if constexpr (B < NB) {
       compute_batch<B % PD>(B);
-      if constexpr (B + PD < NB) load_batch<B % PD>(B + PD);
-      run<B + 1>();
+      if constexpr (B + PD < NB) {
+        load_batch<B % PD>(set, B + PD);
+      }
+      run<B + 1>(set);
     }
   }
 
   // Sum acc over the wave (and the row group's waves through `red`) and
-  // store the row results.
-  __device__ __forceinline__ void finish(float* red, int m) {
+  // store the results of row set `set`.  `red` holds two slots used by
+  // alternate sets: a slot is written again two sets later, after the
+  // barrier of the set in between, which its readers reach only when done.
+  __device__ __forceinline__ void finish(float* red, int m, int set) {
     // after log2(V) butterfly stages lane l holds the sum of value
     // l >> (6 - log2 V) over the lanes that share its upper bits
     constexpr int T = (V >= 32) ? 5 : (V >= 16) ? 4 : (V >= 8) ? 3 : (V >= 4) ? 2 : (V >= 2) ? 1 : 0;
@@ -397,7 +407,7 @@ struct GemvWave {
     const int idx = lane >> (6 - T);
     const bool holder = (lane & ((1 << (6 - T)) - 1)) == 0;
     auto store = [&](int id, float val) {
-      const int row = row0 + id / MT, mm = id % MT;
+      const int row = row0 + set * ROWS + id / MT, mm = id % MT;
       if (row < C.n && mm < m) {
         uint16_t* y = C.y + (size_t)mm * C.n + row;
         if constexpr (BF16) *y = (uint16_t)(pack_bf16x2(val, 0.f) & 0xFFFFu);
@@ -407,11 +417,12 @@ struct GemvWave {
     if (C.wlog == 0) {
       if (holder) store(idx, acc[0]);
     } else {
-      if (holder) red[wave * V + idx] = acc[0];
+      float* slot = red + (set & 1) * (4 * V);
+      if (holder) slot[wave * V + idx] = acc[0];
       __syncthreads();
       if (wsl == 0 && lane < V) {
         float t = 0.f;
-        for (int w = 0; w < (1 << C.wlog); ++w) t += red[(wave + w) * V + lane];
+        for (int w = 0; w < (1 << C.wlog); ++w) t += slot[(wave + w) * V + lane];
         store(lane, t);
       }
     }
@@ -429,7 +440,7 @@ __device__ __forceinline__ void gemv_item(const GemvLaunch& a, const GemvCall& C
   const int lane = (int)(threadIdx.x & 63);
   Wave w(C, it, wave, lane);
   // the weight loads go out first; the activations are read while they fly
-  w.template issue<0>();
+  w.template issue<0>(0);
   uint32_t xw[MT][32];
   if (C.wlog == 0) {
     // chunk j of thread t: piece (t + 256 j) of the [token][slice][piece] X
@@ -471,9 +482,15 @@ __device__ __forceinline__ void gemv_item(const GemvLaunch& a, const GemvCall& C
       }
     }
   }
-  w.x_setup(xw, a.m);
-  w.template run<0>();
-  w.finish(red, a.m);
+  w.x_setup(xw);
+  // a rolled loop: the kernel holds every width's code path, and unrolling
+  // the sets would outgrow the instruction cache
+#pragma unroll 1
+  for (int set = 0; set < C.sets; ++set) {
+    if (set) w.template issue<0>(set);
+    w.template run<0>(set);
+    w.finish(red, a.m, set);
+  }
 }
 
 // One workgroup per item: the item's call is found by a scalar search of the
@@ -481,7 +498,7 @@ __device__ __forceinline__ void gemv_item(const GemvLaunch& a, const GemvCall& C
 // workgroup), so one launch can hold calls of every width.
 template <int RULE, int MT, int BF16, int ROWS>
 __global__ __launch_bounds__(256) void gemv_multi_kernel(GemvLaunch a) {
-  __shared__ float red[4 * ROWS * MT];
+  __shared__ float red[2 * 4 * ROWS * MT];  // two slots of [wave][value]
   __shared__ uint4 xlds[MT * 8 * 64];  // [token][piece][slice] for one-wave rows
   const int it = (int)blockIdx.x;
   int c = 0;
@@ -498,10 +515,20 @@ __global__ __launch_bounds__(256) void gemv_multi_kernel(GemvLaunch a) {
 
 int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 
+// Row sets per item for a launch of `items1` one-set items: two sets spread
+// the activation set-up over twice the rows, one keeps enough workgroups to
+// fill the chip and balance its tail.  Measured on the 8B FFN decode step
+// (7040 one-set items: 1 set 101.7 us, 2 sets 98.6 us, 4 sets 99.4 us) and on
+// its single-width launches (1408 items: 2 sets no faster, 4 sets slower).
+int gemv_sets(int items1) { return items1 >= 4096 ? 2 : 1; }
+
 template <int RULE, int MT, int BF16>
 hipError_t gemv_launch_t(const LinearArgs* la, int ncalls, hipStream_t s) {
   constexpr int ROWS = gemv_rows(MT);
   GemvLaunch a;
+  int items1 = 0;
+  for (int i = 0; i < ncalls; ++i) items1 += cdiv(la[i].n, (4 / waves_per_row(la[i].k)) * ROWS);
+  const int sets = gemv_sets(items1);
   int items = 0;
   for (int i = 0; i < ncalls; ++i) {
     GemvCall& c = a.c[i];
@@ -516,7 +543,8 @@ hipError_t gemv_launch_t(const LinearArgs* la, int ncalls, hipStream_t s) {
     c.item0 = items;
     const int W = waves_per_row(la[i].k);
     c.wlog = W == 1 ? 0 : W == 2 ? 1 : 2;
-    c.rpi = (4 / W) * ROWS;
+    c.sets = sets;
+    c.rpi = (4 / W) * ROWS * sets;
     c.gpr = la[i].k / la[i].group;
     // exact for slice < 256 and group / 64 <= 256: the rounding error of the
     // multiplier stays below 1 / (group / 64)
