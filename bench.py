@@ -5,9 +5,9 @@ Workload (one step): the Llama-3.1-8B FFN projections (gate and up 4096->14336,
 down 14336->4096) at decode batch M = 1, fp16 activations, one int8 parent
 per matrix (g = 128, fp16 scale/zero, W ~ N(0, 0.02^2) with 0.1% outliers x10),
 sliced with the true-prefix rule at every width r in {2, 3, 4, 6, 8}: 15 layer
-calls, issued as one mixed-width call list per width.  Each projection reads a
-fixed seeded input and writes its own output, so the three calls of a width
-are independent and the library runs them as one GEMV launch.
+calls, issued as one mixed-width call list.  Each projection reads a fixed
+seeded input and writes its own output, so the 15 calls are independent and
+the library runs them as one GEMV launch.
 
 Inputs are resident in HBM before timing.  Each step reads a different copy of
 the parents from a ring sized so that every timed piece reads more than 1 GiB
@@ -15,8 +15,9 @@ per pass through it (four times the 256 MB MALL): weight reads come from HBM,
 not the last-level cache.
 
 Timing (one declared mode): the calls are captured in HIP graphs (checked bit
-for bit against eager calls first) and replayed, five decode steps per graph;
-HIP events on the launch stream bracket the replays.
+for bit against eager calls first) and replayed, up to 40 decode steps per
+graph (the default run: one graph of all timed steps); HIP events on the launch
+stream bracket the replays.
   value        algorithmic bytes of all calls of the timed steps / their time
                (GB/s).  Algorithmic bytes per call = bit planes the width reads
                + 4 B (fp16 scale + zero) per group + X (2*M*K) + Y (2*M*N).
@@ -64,7 +65,7 @@ PREFILL_WIDTHS = (2, 4, 8)
 GROUP = 128
 RING_BYTES = 1 << 30           # bytes each timed piece reads per pass through the ring
 MIN_LAUNCHES = 200             # launches averaged per per-launch figure
-GRAPH_STEPS = 5                # decode steps per graph in the timed region
+GRAPH_STEPS = 40               # decode steps per graph in the timed region (the default --steps: one graph)
 METRIC = "sliced W·X: decode GB/s (packed bytes, %HBM peak) + prefill TFLOP/s (%MFMA) per r"
 PLANE_BITS = (2, 1, 1, 2, 2)
 PLANES_FOR_R = {2: 1, 3: 2, 4: 3, 6: 4, 8: 5}
@@ -213,8 +214,10 @@ def main():
     # Graphs of GRAPH_STEPS consecutive steps each (one launch per step),
     # covering the timed steps in order, so exactly --steps steps are timed and
     # consecutive steps read different parent copies.  While the GPU runs one
-    # graph the host submits the next; after the synchronisation that opens
-    # the timed region the GPU waits only for the first (short) submission.
+    # graph the host submits the next.  A replay costs the host tens of
+    # microseconds, which graphs of a few 100-us steps do not hide (graphs of
+    # five steps timed 4.5 us per step above the same launches in a graph of
+    # 66), so the default run replays a single graph of all 40 timed steps.
     segs = [(a, min(a + GRAPH_STEPS, args.steps)) for a in range(0, args.steps, GRAPH_STEPS)]
     step_graphs = [capture(lambda a=a, b=b: [step_calls(i) for i in range(a, b)]) for a, b in segs]
     for gi in sorted({0, len(segs) - 1}):

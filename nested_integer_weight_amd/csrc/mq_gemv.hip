@@ -367,7 +367,9 @@ struct GemvWave {
         } else if constexpr (BF16) {
           t = fmaf(kDelta - z, xs[mm], dot[mm]);
         } else {
-          t = fmaf(-(1024.0f + z - kDelta), xs[mm], dot[mm]);
+          // z + (1024 - delta) is exact (an integer plus a value on a 0.5
+          // grid, below 2^11) and takes one addition
+          t = fmaf(-(z + (1024.0f - kDelta)), xs[mm], dot[mm]);
         }
         acc[(b * RB + i) * MT + mm] = valid ? s * t : 0.f;
       }
