@@ -309,6 +309,39 @@ def test_mixed_heterogeneous_gemv_launch(mq, r, rule, dt):
         check_y(y, lay, lay.x, c.r, c.rule)
 
 
+@pytest.mark.parametrize("m,dt,rule,k,n,ncalls", [
+    (1, "f16", O.PREFIX, 4096, 4100, 32),   # one wave per row, ragged n
+    (1, "f16", O.ROUND, 8192, 4100, 16),    # two waves per row
+    (2, "f16", O.EXTRA, 4096, 4100, 32),    # two tokens
+    (3, "f16", O.PREFIX, 14336, 1030, 32),  # four-token kernel (4 rows per wave) with a padded token, four waves per row
+    (4, "f16", O.ROUND, 4096, 4100, 16),
+    (1, "bf16", O.PREFIX, 4096, 4100, 32),
+    (1, "bf16", O.EXTRA, 14336, 1030, 32),
+])
+def test_gemv_two_row_sets(mq, m, dt, rule, k, n, ncalls):
+    """A GEMV launch of at least 4096 one-set items walks two row sets per
+    item; a single call of these shapes (about 130-260 items) walks one.
+    Every output of the mixed launch equals its single call bit for bit, for
+    every row-group layout, token count, dtype and rule, with n ragged against
+    the two-set item, and the oracle within tolerance."""
+    lay = synth.make_layer(cfg_id=13, tensor_id=m * 10 + RULES.index(rule), n=n, k=k, m=0, group=128, x_dtype=dt)
+    q, s, z = to_dev(lay)
+    pk = mq.pack_parent(q)
+    del q
+    calls = []
+    for i in range(ncalls):
+        r = WIDTHS[i % len(WIDTHS)]
+        x = synth.activations(synth.rng_for(13, 100 + i, m, k), m, k, dt)
+        calls.append(mq.Call(x=x.to(DEV), packed=pk.truncated(r, rule), r=r, rule=rule, group=128, scales=s,
+                             zeros=z))
+    outs = mq.linear_mixed(calls)
+    for c, y in zip(calls, outs):
+        single = mq.linear(c.x, c.packed, c.r, c.rule, c.group, c.scales, c.zeros)
+        assert torch.equal(single, y), (c.r, m, dt, k, n)
+    for i in (0, 4):  # r = 2 and r = 8 against the oracle
+        check_y(outs[i], lay, calls[i].x.cpu(), calls[i].r, rule)
+
+
 @pytest.mark.parametrize("m,dt,r,rule", [(8, "f16", 2, O.PREFIX), (16, "bf16", 3, O.ROUND), (40, "f16", 8, O.PREFIX),
                                          (64, "bf16", 4, O.PREFIX), (5, "f16", 6, O.ROUND)])
 @pytest.mark.parametrize("ws", ["full", "one_split", "none"])
