@@ -11,9 +11,11 @@
 //    groups x sets x ROWS rows; a row group is W waves (W = 1, 2 or 4 by k),
 //    each lane owning a fixed 64-code k-slice of the group's rows, so its
 //    slice of X sits in VGPRs for every row it walks.  A row group walks its
-//    rows in sets of ROWS, one reduction per set; launches with many items
-//    take two sets per item, which halves the share of the activation set-up
-//    per row and still leaves several workgroups per CU.  One 256-thread
+//    rows in sets of ROWS (8, or 4 at four tokens and in launches of few
+//    items, which then have twice the waves), one reduction per set; launches
+//    with many items take two sets per item, which halves the share of the
+//    activation set-up per row and still leaves several workgroups per CU.
+//    One 256-thread
 //    workgroup per item; a launch covers the items of up to kGemvMaxCalls
 //    calls of one rule, m and dtype (any width, n, k and group), found by a
 //    scalar search of the kernel arguments; the call's width selects the
@@ -81,7 +83,7 @@ __host__ __device__ inline int waves_per_row(int k) {
 }
 
 // Rows per wave: eight, or four for four tokens (the transposing butterfly
-// reduces ROWS x tokens <= 32 values per lane).
+// reduces ROWS x tokens <= 32 values per lane) and in launches of few items.
 __host__ __device__ constexpr int gemv_rows(int mt) { return mt >= 4 ? 4 : 8; }
 
 // Transposing butterfly stage with xor-offset O on VC values per lane.
@@ -524,13 +526,9 @@ int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 // its single-width launches (1408 items: 2 sets no faster, 4 sets slower).
 int gemv_sets(int items1) { return items1 >= 4096 ? 2 : 1; }
 
-template <int RULE, int MT, int BF16>
-hipError_t gemv_launch_t(const LinearArgs* la, int ncalls, hipStream_t s) {
-  constexpr int ROWS = gemv_rows(MT);
+template <int RULE, int MT, int BF16, int ROWS>
+hipError_t gemv_launch_r(const LinearArgs* la, int ncalls, int sets, hipStream_t s) {
   GemvLaunch a;
-  int items1 = 0;
-  for (int i = 0; i < ncalls; ++i) items1 += cdiv(la[i].n, (4 / waves_per_row(la[i].k)) * ROWS);
-  const int sets = gemv_sets(items1);
   int items = 0;
   for (int i = 0; i < ncalls; ++i) {
     GemvCall& c = a.c[i];
@@ -558,6 +556,27 @@ hipError_t gemv_launch_t(const LinearArgs* la, int ncalls, hipStream_t s) {
   a.m = la[0].m;
   hipLaunchKernelGGL((gemv_multi_kernel<RULE, MT, BF16, ROWS>), dim3((unsigned)items), dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+// Launches of few items (fewer than kGemvFewItems 8-row items) take 4-row
+// waves: twice the waves, and so twice the loads in flight, for the same bytes.
+// Measured: the Llama-3.1-8B attention projections at M = 1 (q, k, v and o in
+// one launch, 320 items) 4-8% faster at r >= 3 (4% slower at r = 2, where the
+// per-item set-up weighs more), their dependent q/k/v-then-o block up to 15%
+// faster; the FFN down (512 items, four waves per row) and gate+up (896)
+// launches 2-15% slower.  A lane's partial sums meet in the same butterfly
+// tree at either row count, so results do not depend on the choice.
+constexpr int kGemvFewItems = 448;
+
+template <int RULE, int MT, int BF16>
+hipError_t gemv_launch_t(const LinearArgs* la, int ncalls, hipStream_t s) {
+  constexpr int ROWS = gemv_rows(MT);
+  int items1 = 0;
+  for (int i = 0; i < ncalls; ++i) items1 += cdiv(la[i].n, (4 / waves_per_row(la[i].k)) * ROWS);
+  if constexpr (ROWS == 8) {
+    if (items1 < kGemvFewItems) return gemv_launch_r<RULE, MT, BF16, 4>(la, ncalls, 1, s);
+  }
+  return gemv_launch_r<RULE, MT, BF16, ROWS>(la, ncalls, gemv_sets(items1), s);
 }
 
 template <int RULE, int BF16>
