@@ -61,8 +61,9 @@
  *   y       [m, n] row-major, same dtype as x; overwritten, not accumulated.
  *
  * Shape rules: n >= 1, k >= 64, k % 64 == 0, group % 64 == 0, k % group == 0,
- * n * k <= 2^40 (MQ_ESIZE), m >= 0 (m == 0 is a no-op).  Every device pointer
- * must be 16-byte aligned.
+ * n * k <= 2^40 (MQ_ESIZE), m >= 0 (m == 0 is a no-op); the layer calls
+ * (mq_linear, mq_linear_noalloc, mq_linear_mixed) also need k <= 2^22
+ * (MQ_ESIZE).  Every device pointer must be 16-byte aligned.
  *
  * Ownership and threading: the caller allocates and owns every buffer,
  * including the optional split-K workspace of mq_linear.  The library

@@ -75,6 +75,8 @@ mq_status validate_linear(const void* x, int x_dtype, int m, const mq_packed* w,
   // kernels index with 64-bit offsets; keep grid dimensions in range
   if ((long long)m * (long long)w->n > (1LL << 46) || (long long)w->n * (long long)w->k > (1LL << 46))
     return MQ_ESIZE;
+  // the GEMM addresses a workgroup's 256 activation rows with 32-bit byte offsets
+  if (w->k > kMaxLinearK) return MQ_ESIZE;
   return MQ_OK;
 }
 

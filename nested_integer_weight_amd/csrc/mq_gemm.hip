@@ -8,9 +8,13 @@
 //    an integer zero point), rounds once to the activation dtype and writes
 //    the tile to LDS,
 //  * runs v_mfma_f32_16x16x32_{bf16,f16} from LDS with fp32 accumulators.
-// LDS is double buffered: the next step's global loads are issued before the
-// current step's MFMAs and its dequantization is written to the other buffer
-// afterwards, so one barrier per step suffices.
+// LDS is double buffered, so one barrier per step suffices: a step computes
+// from one buffer pair while the next step's tiles are written to the other.
+// In the eight-wave prefill tile half the waves stage the next step before
+// their MFMAs and half after, so on every SIMD one wave's dequantization
+// overlaps the other wave's matrix work.  Operands are read with buffer loads
+// from per-workgroup windows (scalar bases, fixed 32-bit lane offsets, the k
+// step in the scalar offset).
 //
 // This is the pages' fused dequantize-and-multiply design for prefill and
 // larger batches (MatGPTQ "Efficient and Accurate Inference over Nested
@@ -66,6 +70,18 @@ __device__ __forceinline__ floatx4 mfma16x16x32(const uint4& a, const uint4& b, 
   }
 }
 
+// Raw buffer descriptor of a workgroup's window of an operand: the base in
+// scalar registers (read-first-lane), no stride, 4 GiB - 1 bytes.  Lanes then
+// address the window with 32-bit byte offsets that stay fixed over the k loop,
+// and the k step goes into the scalar offset, so the loop keeps no 64-bit
+// addresses in vector registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t window_rsrc(const void* base) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(lo | (hi << 32)), (short)0, -1, 0x00020000);
+}
+
 // Per-thread state of one workgroup tile.  Helpers are force-inlined member
 // functions (not lambdas capturing arrays by reference), so the staging
 // arrays are scalarised into registers instead of living in memory.
@@ -80,80 +96,85 @@ struct GemmTile {
   static_assert(CW >= 1 && CW * T == BN * 2, "W tile split");
   static constexpr float kDelta = RULE ? 0.0f : prefix_delta(R);
 
-  const GemmArgs& a;
-  int tid, m0, n0, gpr;
-  size_t upr;
-  // staging registers: the X tile one k step ahead, the weight planes (from
-  // HBM, longer latency) two steps ahead in two slots
-  // X staging slots: two (X issued two steps ahead) when the register budget
-  // allows it, i.e. for widths with at most three planes; one otherwise
-  static constexpr int XD = NP <= 3 ? 2 : 1;
-  uint4 xreg[XD][CX];
+  int tid;
+  // descriptors of the workgroup's windows (X rows from m0, weight rows from n0)
+  __amdgpu_buffer_rsrc_t rx, rp[NP], rs, rz;
+  int xoff[CX];           // byte offset of the thread's X chunks in the window at k = 0
+  int woff[CW], goff[CW];  // byte offsets of its weight items (1-bit plane units) and their groups
+  int gsteps;              // k steps per group
+  // staging registers: the X tile one k step ahead, the weight planes two
+  // steps ahead in two slots
+  uint4 xreg[CX];
   uint32_t wrec[2][CW][kUnitWords];
   uint16_t sraw[2][CW], zraw[2][CW];
   floatx4 acc[FM][FN];
 
-  __device__ __forceinline__ GemmTile(const GemmArgs& args, int t, int m0_, int n0_) : a(args), tid(t), m0(m0_), n0(n0_) {
-    upr = (size_t)(a.k >> 5);
-    gpr = a.k / a.group;
+  __device__ __forceinline__ GemmTile(const GemmArgs& a, int t, int m0, int n0) : tid(t) {
+    const int upr = a.k >> 5, gpr = a.k / a.group;
+    rx = window_rsrc(static_cast<const uint16_t*>(a.x) + (size_t)m0 * a.k);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) rp[p] = window_rsrc(a.pl.p[p] + (size_t)n0 * upr * kPlaneBits[p]);
+    rs = window_rsrc(a.scales + (size_t)n0 * gpr);
+    rz = window_rsrc(a.zeros + (size_t)n0 * gpr);
+    // X chunk c (16 B) is row c / 8, k 8 (c % 8) .. + 7: eight consecutive
+    // lanes read one row's 128-byte k slice.  Rows past m are clamped to
+    // m - 1: they only feed output rows that are never stored.
+#pragma unroll
+    for (int i = 0; i < CX; ++i) {
+      const int c = (tid + i * T) % (BM * 8);
+      const int row = min(c >> 3, a.m - 1 - m0);
+      xoff[i] = (row * a.k + 8 * (c & 7)) * 2;
+    }
+    // weight item it -> (row it / 2, unit it % 2): a lane pair reads one
+    // row's two units, i.e. 16 contiguous bytes of a 2-bit plane; rows past n
+    // are clamped (their output columns are never stored)
+#pragma unroll
+    for (int i = 0; i < CW; ++i) {
+      const int it = tid + i * T;
+      const int row = min(it >> 1, a.n - 1 - n0);
+      woff[i] = (row * upr + (it & 1)) * 4;
+      goff[i] = row * gpr * 2;
+    }
+    gsteps = a.group / BK;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // X chunk c (16 B) is row c / 8, k 8 (c % 8) .. + 7: eight consecutive lanes
-  // read one row's 128-byte k slice, so the vector cache sees one request per
-  // row instead of one per lane.  Unconditional loads from clamped addresses:
-  // X rows past m only feed output rows that are never stored.
-  template <int XS>
   __device__ __forceinline__ void load_x(int kt) {
-    const int k0 = kt * BK;
-    const uint16_t* xg = static_cast<const uint16_t*>(a.x);
 #pragma unroll
-    for (int i = 0; i < CX; ++i) {
-      const int c = (tid + i * T) % (BM * 8);
-      const int row = c >> 3, col = 8 * (c & 7);
-      const int mrow = min(m0 + row, a.m - 1);
-      xreg[XS % XD][i] = *reinterpret_cast<const uint4*>(xg + (size_t)mrow * a.k + k0 + col);
-    }
+    for (int i = 0; i < CX; ++i)
+      xreg[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff[i], kt * BK * 2, 0));
   }
   // the X tile in LDS is row-major, eight 16-byte chunks per row, with chunk
   // c of row r stored at position c ^ (r % 8): the staging writes (eight
   // lanes per row) and the MFMA fragment reads (sixteen rows, one chunk
   // each) then both spread over all banks
-  template <int XS>
   __device__ __forceinline__ void store_x(uint4* as) {
 #pragma unroll
     for (int i = 0; i < CX; ++i) {
       const int c = tid + i * T;
-      if ((BM * 8) % T == 0 || c < BM * 8) as[(c >> 3) * 8 + ((c & 7) ^ ((c >> 3) & 7))] = xreg[XS % XD][i];
+      if ((BM * 8) % T == 0 || c < BM * 8) as[(c >> 3) * 8 + ((c & 7) ^ ((c >> 3) & 7))] = xreg[i];
     }
   }
-  // weight item it -> (row it / 2, unit it % 2): a lane pair reads one row's two
-  // units, i.e. 16 contiguous bytes of a 2-bit plane
   template <int SLOT>
   __device__ __forceinline__ void load_w(int kt) {
-    const int gk = (kt * BK) / a.group;
+    const int gk = kt / gsteps;
 #pragma unroll
     for (int i = 0; i < CW; ++i) {
-      const int it = tid + i * T;
-      const int row = it >> 1, u = it & 1;
-      const int nrow = min(n0 + row, a.n - 1);  // clamped; the output column is never stored
-      const size_t unit = (size_t)nrow * upr + (size_t)(kt * 2 + u);
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
         if (kPlaneBits[p] == 2) {
-          uint2 v = reinterpret_cast<const uint2*>(a.pl.p[p])[unit];
-          wrec[SLOT][i][kUnitOff[p]] = v.x;
-          wrec[SLOT][i][kUnitOff[p] + 1] = v.y;
+          const auto v = __builtin_amdgcn_raw_buffer_load_b64(rp[p], woff[i] * 2, kt * 16, 0);
+          wrec[SLOT][i][kUnitOff[p]] = v[0];
+          wrec[SLOT][i][kUnitOff[p] + 1] = v[1];
         } else {
-          wrec[SLOT][i][kUnitOff[p]] = a.pl.p[p][unit];
+          wrec[SLOT][i][kUnitOff[p]] = __builtin_amdgcn_raw_buffer_load_b32(rp[p], woff[i], kt * 8, 0);
         }
       }
-      const size_t g = (size_t)nrow * gpr + (size_t)gk;
-      sraw[SLOT][i] = a.scales[g];
-      zraw[SLOT][i] = a.zeros[g];
+      sraw[SLOT][i] = __builtin_amdgcn_raw_buffer_load_b16(rs, goff[i], gk * 2, 0);
+      zraw[SLOT][i] = __builtin_amdgcn_raw_buffer_load_b16(rz, goff[i], gk * 2, 0);
     }
   }
   // rebuild, slice and dequantize (exactly, in fp32) the staged weights, round
@@ -198,9 +219,10 @@ struct GemmTile {
       dst[48] = make_uint4(h[12], h[13], h[14], h[15]);
     }
   }
-  // MFMAs of one 32-wide k half from LDS tiles as[BM][8], bs[BN/16][2][64]
-  __device__ __forceinline__ void mma_half(const uint4* as, const uint4* bs, int kh, int lane, int wm, int wn) {
-    {
+  // the MFMAs of one 64-wide k step from LDS tiles as[BM][8], bs[BN/16][2][64]
+  __device__ __forceinline__ void mma(const uint4* as, const uint4* bs, int lane, int wm, int wn) {
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
       uint4 bfr[FN];
 #pragma unroll
       for (int j = 0; j < FN; ++j) bfr[j] = bs[((wn * FN + j) * 2 + kh) * 64 + (lane ^ (4 * kh))];
@@ -212,19 +234,86 @@ struct GemmTile {
       }
     }
   }
+
+  // The k loop over [kb, ke), two steps per trip so the LDS buffer and the
+  // staging slots are compile-time constants; one barrier per step.  Step kt
+  // computes from buffers kt & 1 (As[b], Bs[b] with b relative to kb) and
+  // writes step kt + 1 (X loaded a step earlier, weights two) into the other
+  // pair.  Past the last step the loads repeat the last step (in bounds) and
+  // the stores go to the pair no later step reads.
+  //
+  // compute_first: every step issues its loads, runs its MFMAs, then stages.
+  // stage_first: every step stages, issues its loads, then runs its MFMAs.
+  // Waves of the two orders on one SIMD overlap one wave's staging with the
+  // other's MFMAs; both touch only the pair the order assigns to the step.
+  __device__ __forceinline__ void compute_first(uint4* as0, uint4* as1, uint4* bs0, uint4* bs1, int kb, int ke,
+                                                int lane, int wm, int wn) {
+    const int kl = ke - 1;
+    load_w<0>(kb);
+    load_x(kb);
+    load_w<1>(min(kb + 1, kl));
+    store_x(as0);
+    store_w<0>(bs0);
+    __syncthreads();
+    for (int kt = kb; kt < ke; kt += 2) {
+      load_x(min(kt + 1, kl));
+      load_w<0>(min(kt + 2, kl));
+      mma(as0, bs0, lane, wm, wn);
+      store_x(as1);
+      store_w<1>(bs1);
+      __syncthreads();
+      if (kt + 1 < ke) {
+        load_x(min(kt + 2, kl));
+        load_w<1>(min(kt + 3, kl));
+        mma(as1, bs1, lane, wm, wn);
+        store_x(as0);
+        store_w<0>(bs0);
+        __syncthreads();
+      }
+    }
+  }
+  __device__ __forceinline__ void stage_first(uint4* as0, uint4* as1, uint4* bs0, uint4* bs1, int kb, int ke,
+                                              int lane, int wm, int wn) {
+    const int kl = ke - 1;
+    load_w<0>(kb);
+    load_x(kb);
+    load_w<1>(min(kb + 1, kl));
+    store_x(as0);
+    store_w<0>(bs0);
+    load_x(min(kb + 1, kl));
+    __syncthreads();
+    for (int kt = kb; kt < ke; kt += 2) {
+      store_x(as1);
+      store_w<1>(bs1);
+      load_x(min(kt + 2, kl));
+      load_w<0>(min(kt + 2, kl));
+      mma(as0, bs0, lane, wm, wn);
+      __syncthreads();
+      if (kt + 1 < ke) {
+        store_x(as0);
+        store_w<0>(bs0);
+        load_x(min(kt + 3, kl));
+        load_w<1>(min(kt + 3, kl));
+        mma(as1, bs1, lane, wm, wn);
+        __syncthreads();
+      }
+    }
+  }
 };
 
-template <int R, int RULE, int BF16, int BM, int BN, int WM, int WN>
+// PP = 1 (eight-wave tiles): waves 4..7 take the stage-first order, so each
+// SIMD holds one wave of either order (waves are placed on the SIMDs in turn).
+template <int R, int RULE, int BF16, int BM, int BN, int WM, int WN, int PP>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs a) {
   using Tile = GemmTile<R, RULE, BF16, BM, BN, WM, WN>;
-  constexpr int FM = Tile::FM, FN = Tile::FN;
+  static_assert(!PP || WM * WN == 8, "two orders need two waves per SIMD");
   // double-buffered LDS tiles: X swizzled row-major, weights fragment-major
   __shared__ uint4 As[2][BM * 8];
   __shared__ uint4 Bs[2][BN / 16 * 2 * 64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % WM, wn = wave / WM;
 
   // ---- tile selection: workgroups sharing a weight tile land on one XCD ----
@@ -238,55 +327,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs a) {
   const int kt_begin = blockIdx.y * a.ksteps_per_split;
   const int kt_end = min(KT, kt_begin + a.ksteps_per_split);
 
+  // every k range is non-empty (the launcher sizes grid.y so)
   Tile t(a, tid, m0, n0);
-
-  if (kt_begin < kt_end) {
-    const int klast = kt_end - 1;
-    constexpr int XD = Tile::XD;
-    t.template load_w<0>(kt_begin);
-    t.template load_x<0>(kt_begin);
-    t.template load_w<1>(min(kt_begin + 1, klast));
-    if constexpr (XD == 2) t.template load_x<1>(min(kt_begin + 1, klast));
-    t.template store_x<0>(As[0]);
-    t.template store_w<0>(Bs[0]);
-    __syncthreads();
-    // Two k steps per trip so the LDS buffer and the staging slots are
-    // compile-time constants.  Step kt computes from buffer kt & 1, issues the
-    // weights for kt + 2 (into the slot that held kt) and X for kt + XD, then
-    // writes step kt + 1 (weights loaded a step earlier, X loaded XD - 1 steps
-    // earlier) into the other buffer.  Past the last step the loads repeat
-    // the last step (in bounds) and nothing more is stored.
-    for (int kt = kt_begin; kt < kt_end; kt += 2) {
-      {
-        const bool has_next = kt + 1 < kt_end;
-        if constexpr (XD == 2) t.template load_x<0>(min(kt + 2, klast));
-        else if (has_next) t.template load_x<0>(kt + 1);
-        t.template load_w<0>(min(kt + 2, klast));
-        t.mma_half(As[0], Bs[0], 0, lane, wm, wn);
-        t.mma_half(As[0], Bs[0], 1, lane, wm, wn);
-        if (has_next) {
-          t.template store_x<1>(As[1]);
-          t.template store_w<1>(Bs[1]);
-        }
-        __syncthreads();
-      }
-      if (kt + 1 < kt_end) {
-        const bool has_next = kt + 2 < kt_end;
-        if constexpr (XD == 2) t.template load_x<1>(min(kt + 3, klast));
-        else if (has_next) t.template load_x<0>(kt + 2);
-        t.template load_w<1>(min(kt + 3, klast));
-        t.mma_half(As[1], Bs[1], 0, lane, wm, wn);
-        t.mma_half(As[1], Bs[1], 1, lane, wm, wn);
-        if (has_next) {
-          t.template store_x<0>(As[0]);
-          t.template store_w<0>(Bs[0]);
-        }
-        __syncthreads();
-      }
-    }
-  }
+  if (PP && (wave >> 2) == 1)
+    t.stage_first(As[0], As[1], Bs[0], Bs[1], kt_begin, kt_end, lane, wm, wn);
+  else
+    t.compute_first(As[0], As[1], Bs[0], Bs[1], kt_begin, kt_end, lane, wm, wn);
 
   // ---- epilogue: lane holds D[4*(lane/16) + v][lane % 16] of each block ----
+  constexpr int FM = Tile::FM, FN = Tile::FN;
   const int mbase = m0 + wm * (BM / WM) + (lane >> 4) * 4;
   const int nbase = n0 + wn * (BN / WN) + (lane & 15);
 #pragma unroll
@@ -343,7 +392,7 @@ struct TileCfg {
   int bm, bn;
 };
 constexpr TileCfg kCfgs[] = {
-    {256, 256},  // 0: prefill, 8 waves (2 x 4), wave tile 128 x 64
+    {256, 256},  // 0: prefill, 8 waves (4 x 2), wave tile 64 x 128, two step orders
     {128, 256},  // 1: 8 waves (2 x 4), wave tile 64 x 64
     {64, 256},   // 2: 4 waves (1 x 4), wave tile 64 x 64
     {32, 256},   // 3: 4 waves (1 x 4), wave tile 32 x 64
@@ -416,17 +465,17 @@ GemmPlan plan_gemm(int m, int n, int k, size_t workspace_bytes) {
   return p;
 }
 
-template <int R, int RULE, int BF16, int BM, int BN, int WM, int WN>
+template <int R, int RULE, int BF16, int BM, int BN, int WM, int WN, int PP = 0>
 static hipError_t gemm_launch_cfg(const GemmArgs& ga, int splits, hipStream_t s) {
   dim3 grid((unsigned)(ga.tiles_m * ga.tiles_n), (unsigned)splits);
-  hipLaunchKernelGGL((gemm_kernel<R, RULE, BF16, BM, BN, WM, WN>), grid, dim3(64 * WM * WN), 0, s, ga);
+  hipLaunchKernelGGL((gemm_kernel<R, RULE, BF16, BM, BN, WM, WN, PP>), grid, dim3(64 * WM * WN), 0, s, ga);
   return hipGetLastError();
 }
 
 template <int R, int RULE, int BF16>
 static hipError_t gemm_launch_t(const GemmArgs& ga, int cfg, int splits, hipStream_t s) {
   switch (cfg) {
-    case 0: return gemm_launch_cfg<R, RULE, BF16, 256, 256, 2, 4>(ga, splits, s);
+    case 0: return gemm_launch_cfg<R, RULE, BF16, 256, 256, 4, 2, 1>(ga, splits, s);
     case 1: return gemm_launch_cfg<R, RULE, BF16, 128, 256, 2, 4>(ga, splits, s);
     case 2: return gemm_launch_cfg<R, RULE, BF16, 64, 256, 1, 4>(ga, splits, s);
     case 3: return gemm_launch_cfg<R, RULE, BF16, 32, 256, 1, 4>(ga, splits, s);
@@ -454,8 +503,10 @@ hipError_t launch_gemm(const LinearArgs& la, const GemmPlan& plan, void* workspa
   ga.tiles_m = cdiv(la.m, kCfgs[plan.cfg].bm);
   ga.tiles_n = cdiv(la.n, kCfgs[plan.cfg].bn);
   const int KT = la.k / BK;
-  const int splits = plan.splits;
-  ga.ksteps_per_split = cdiv(KT, splits);
+  // k ranges of cdiv(KT, plan.splits) steps; only as many as hold a step
+  // (at most plan.splits, so the workspace is large enough)
+  ga.ksteps_per_split = cdiv(KT, plan.splits);
+  const int splits = cdiv(KT, ga.ksteps_per_split);
   ga.to_workspace = splits > 1;
   ga.y = splits > 1 ? workspace : la.y;
   hipError_t e;

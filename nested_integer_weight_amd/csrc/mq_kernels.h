@@ -74,7 +74,9 @@ hipError_t launch_skinny_multi(const LinearArgs* a, int ncalls, void* workspace,
 // fixed-order sum of fp32 split-k partials ws[splits][mn] rounded once into y (fp16 or bf16)
 hipError_t launch_splitk_reduce(const float* ws, int splits, size_t mn, void* y, int bf16, hipStream_t s);
 
-// MFMA GEMM (dequantized weight tiles in LDS), any m >= 1.
+// MFMA GEMM (dequantized weight tiles in LDS), any m >= 1, k <= kMaxLinearK
+// (its 32-bit byte offsets into a 256-row activation window).
+constexpr int kMaxLinearK = 1 << 22;
 struct GemmPlan {
   int cfg;       // tile configuration index
   int splits;    // split-k factor (1 = no workspace)

@@ -84,6 +84,7 @@ def _linear(L, x=4096, dt=1, m=1, w=None, r=4, rule=0, group=64, s=4096, z=8192,
     (dict(w=_packed(planes=(16, 32, 48, 0, 80)), r=4, rule=1), 5),
     (dict(w=_packed(planes=(18, 32, 48, 64, 80))), 4),
     (dict(dt=0), 6), (dict(dt=7), 6),
+    (dict(w=_packed(k=(1 << 22) + 64)), 9),
 ])
 def test_linear_validation(L, kw, status):
     assert _linear(L, **kw) == status
