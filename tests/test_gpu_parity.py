@@ -160,6 +160,9 @@ SHAPES = [
     (300, 448, 1024, 128, "bf16"),  # prefill tile with split k
     (257, 672, 2048, 64, "f16"),    # prefill tile, ragged m, group 64
     (300, 520, 1024, 128, "f16"),
+    (200, 100, 64, 64, "f16"),      # prefill tile, a single k step
+    (260, 300, 576, 64, "f16"),     # prefill tile, nine k steps (odd: the last trip runs one step)
+    (300, 300, 1344, 64, "bf16"),   # prefill tile, k split into ranges of 11 and 10 steps
 ]
 
 
