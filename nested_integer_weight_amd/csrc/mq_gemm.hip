@@ -37,6 +37,7 @@ namespace mq {
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int BK = 64;
 // The weight tile in LDS is fragment-major: a 16-row x 32-k block is 1 KB and
@@ -198,16 +199,38 @@ struct GemmTile {
       bytes[6] = assemble_word<NP, 6>(rec);
       bytes[7] = assemble_word<NP, 7>(rec);
       uint32_t h[16];
+      if constexpr (RULE != kRuleExtra || R == 8) {
+        // slice values v <= 255: v_perm puts each byte under an fp16 exponent
+        // byte, giving the exact halves 1024 + v, and one fma per weight with
+        // the 1024 folded into the constant, (1024 + v) s + (cz - 1024 s),
+        // gives v s + cz exactly (the constant needs at most 24 significant
+        // bits, the result at most 21)
+        const float c1 = cz - 1024.0f * s;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float v[4];
-        slice_f32x4<R, RULE>(bytes[j], v);
-        const float w0 = fmaf(v[0], s, cz);
-        const float w1 = fmaf(v[1], s, cz);
-        const float w2 = fmaf(v[2], s, cz);
-        const float w3 = fmaf(v[3], s, cz);
-        h[2 * j] = BF16 ? pack_bf16x2(w0, w1) : pack_f16x2(w0, w1);
-        h[2 * j + 1] = BF16 ? pack_bf16x2(w2, w3) : pack_f16x2(w2, w3);
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t w = slice_bytes<R, RULE>(bytes[j]);
+          const f16x2_t p0 = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, w, 0x04010400u));
+          const f16x2_t p1 = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, w, 0x04030402u));
+          const float w0 = fmaf((float)p0[0], s, c1);
+          const float w1 = fmaf((float)p0[1], s, c1);
+          const float w2 = fmaf((float)p1[0], s, c1);
+          const float w3 = fmaf((float)p1[1], s, c1);
+          h[2 * j] = BF16 ? pack_bf16x2(w0, w1) : pack_f16x2(w0, w1);
+          h[2 * j + 1] = BF16 ? pack_bf16x2(w2, w3) : pack_f16x2(w2, w3);
+        }
+      } else {
+        // the unclamped slice reaches 256: through fp32 lanes
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          float v[4];
+          slice_f32x4<R, RULE>(bytes[j], v);
+          const float w0 = fmaf(v[0], s, cz);
+          const float w1 = fmaf(v[1], s, cz);
+          const float w2 = fmaf(v[2], s, cz);
+          const float w3 = fmaf(v[3], s, cz);
+          h[2 * j] = BF16 ? pack_bf16x2(w0, w1) : pack_f16x2(w0, w1);
+          h[2 * j + 1] = BF16 ? pack_bf16x2(w2, w3) : pack_f16x2(w2, w3);
+        }
       }
       // 8-k chunk j of this row's k half u is lane (row % 16) + 16 j of block (row / 16, u)
       // (positions in the second k half are xor-ed with 4 so that the lane
