@@ -103,11 +103,15 @@ struct GemmTile {
   int xoff[CX];           // byte offset of the thread's X chunks in the window at k = 0
   int woff[CW], goff[CW];  // byte offsets of its weight items (1-bit plane units) and their groups
   int gsteps;              // k steps per group
+  int kfirst;              // first k step of the workgroup's range
   // staging registers: the X tile one k step ahead, the weight planes two
   // steps ahead in two slots
   uint4 xreg[CX];
   uint32_t wrec[2][CW][kUnitWords];
   uint16_t sraw[2][CW], zraw[2][CW];
+  // scale and zero point of the last step written to LDS: a step in the same
+  // group as its predecessor takes them from here instead of loading them
+  uint16_t scur[CW], zcur[CW];
   floatx4 acc[FM][FN];
 
   __device__ __forceinline__ GemmTile(const GemmArgs& a, int t, int m0, int n0) : tid(t) {
@@ -137,6 +141,9 @@ struct GemmTile {
       goff[i] = row * gpr * 2;
     }
     gsteps = a.group / BK;
+    kfirst = 0;
+#pragma unroll
+    for (int i = 0; i < CW; ++i) scur[i] = zcur[i] = 0;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -159,9 +166,12 @@ struct GemmTile {
       if ((BM * 8) % T == 0 || c < BM * 8) as[(c >> 3) * 8 + ((c & 7) ^ ((c >> 3) & 7))] = xreg[i];
     }
   }
+  // does step kt start a group (or the range), so that it loads its own scale and zero point?
+  __device__ __forceinline__ bool own_sz(int kt) const { return kt == kfirst || kt % gsteps == 0; }
   template <int SLOT>
   __device__ __forceinline__ void load_w(int kt) {
     const int gk = kt / gsteps;
+    const bool sz = own_sz(kt);
 #pragma unroll
     for (int i = 0; i < CW; ++i) {
 #pragma unroll
@@ -174,20 +184,28 @@ struct GemmTile {
           wrec[SLOT][i][kUnitOff[p]] = __builtin_amdgcn_raw_buffer_load_b32(rp[p], woff[i], kt * 8, 0);
         }
       }
-      sraw[SLOT][i] = __builtin_amdgcn_raw_buffer_load_b16(rs, goff[i], gk * 2, 0);
-      zraw[SLOT][i] = __builtin_amdgcn_raw_buffer_load_b16(rz, goff[i], gk * 2, 0);
+      if (sz) {
+        sraw[SLOT][i] = __builtin_amdgcn_raw_buffer_load_b16(rs, goff[i], gk * 2, 0);
+        zraw[SLOT][i] = __builtin_amdgcn_raw_buffer_load_b16(rz, goff[i], gk * 2, 0);
+      }
     }
   }
   // rebuild, slice and dequantize (exactly, in fp32) the staged weights, round
   // once to the MFMA dtype and write them to the LDS tile bs[BN/16][2][64]
+  // (step kt: the step whose weights slot SLOT holds; steps are written in order)
   template <int SLOT>
-  __device__ __forceinline__ void store_w(uint4* bs) {
+  __device__ __forceinline__ void store_w(uint4* bs, int kt) {
+    const bool sz = own_sz(kt);
 #pragma unroll
     for (int i = 0; i < CW; ++i) {
       const int it = tid + i * T;
       const int row = it >> 1, u = it & 1;
-      const float s = h2f(sraw[SLOT][i]);
-      const float cz = (kDelta - h2f(zraw[SLOT][i])) * s;  // exact
+      if (sz) {
+        scur[i] = sraw[SLOT][i];
+        zcur[i] = zraw[SLOT][i];
+      }
+      const float s = h2f(scur[i]);
+      const float cz = (kDelta - h2f(zcur[i])) * s;  // exact
       const uint32_t* rec = wrec[SLOT][i];
       uint32_t bytes[8];
       bytes[0] = assemble_word<NP, 0>(rec);
@@ -272,25 +290,26 @@ struct GemmTile {
   __device__ __forceinline__ void compute_first(uint4* as0, uint4* as1, uint4* bs0, uint4* bs1, int kb, int ke,
                                                 int lane, int wm, int wn) {
     const int kl = ke - 1;
+    kfirst = kb;
     load_w<0>(kb);
     load_x(kb);
     load_w<1>(min(kb + 1, kl));
     store_x(as0);
-    store_w<0>(bs0);
+    store_w<0>(bs0, kb);
     __syncthreads();
     for (int kt = kb; kt < ke; kt += 2) {
       load_x(min(kt + 1, kl));
       load_w<0>(min(kt + 2, kl));
       mma(as0, bs0, lane, wm, wn);
       store_x(as1);
-      store_w<1>(bs1);
+      store_w<1>(bs1, min(kt + 1, kl));
       __syncthreads();
       if (kt + 1 < ke) {
         load_x(min(kt + 2, kl));
         load_w<1>(min(kt + 3, kl));
         mma(as1, bs1, lane, wm, wn);
         store_x(as0);
-        store_w<0>(bs0);
+        store_w<0>(bs0, min(kt + 2, kl));
         __syncthreads();
       }
     }
@@ -298,23 +317,24 @@ struct GemmTile {
   __device__ __forceinline__ void stage_first(uint4* as0, uint4* as1, uint4* bs0, uint4* bs1, int kb, int ke,
                                               int lane, int wm, int wn) {
     const int kl = ke - 1;
+    kfirst = kb;
     load_w<0>(kb);
     load_x(kb);
     load_w<1>(min(kb + 1, kl));
     store_x(as0);
-    store_w<0>(bs0);
+    store_w<0>(bs0, kb);
     load_x(min(kb + 1, kl));
     __syncthreads();
     for (int kt = kb; kt < ke; kt += 2) {
       store_x(as1);
-      store_w<1>(bs1);
+      store_w<1>(bs1, min(kt + 1, kl));
       load_x(min(kt + 2, kl));
       load_w<0>(min(kt + 2, kl));
       mma(as0, bs0, lane, wm, wn);
       __syncthreads();
       if (kt + 1 < ke) {
         store_x(as0);
-        store_w<0>(bs0);
+        store_w<0>(bs0, min(kt + 2, kl));
         load_x(min(kt + 3, kl));
         load_w<1>(min(kt + 3, kl));
         mma(as1, bs1, lane, wm, wn);
