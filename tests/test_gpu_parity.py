@@ -193,6 +193,29 @@ def test_linear_shapes(mq, m, n, k, group, dt, r, rule):
     check_y(y, lay, lay.x, r, rule)
 
 
+# The largest k a layer call takes (2^22): the GEMM addresses its activation
+# and weight windows with 32-bit byte offsets, which reach their widest here.
+# Sampled output columns (all rows) against the fp64 oracle.
+@pytest.mark.parametrize("m,dt", [(1, "bf16"), (2, "f16"), (129, "bf16")], ids=["gemm-m1", "skinny-m2", "prefill-tile-m129"])
+def test_linear_max_k(mq, m, dt):
+    k, n, group = 1 << 22, 72, 128
+    lay = synth.make_layer(cfg_id=6, tensor_id=9000 + m, n=n, k=k, m=m, group=group, x_dtype=dt)
+    q, s, z = to_dev(lay)
+    pk = mq.pack_parent(q)
+    del q
+    x = lay.x.to(DEV)
+    cols = [0, 1, 37, n - 1]
+    xn = np.concatenate([np.linalg.norm(lay.x[i:i + 16].double().numpy(), axis=1) for i in range(0, m, 16)])
+    for r in (2, 8):
+        y = mq.linear(x, pk.truncated(r), r, O.PREFIX, group, s, z)
+        y = y.float().cpu().numpy().astype(np.float64)[:, cols]
+        w64 = O.dequant(lay.q[cols], lay.scales[cols], lay.zeros[cols], r, O.PREFIX, group)
+        y_ref = np.concatenate([lay.x[i:i + 16].double().numpy() @ w64.T for i in range(0, m, 16)])
+        assert np.all(np.isfinite(y))
+        err = np.max(np.abs(y - y_ref) / (xn[:, None] * np.linalg.norm(w64, axis=1)[None, :]))
+        assert err <= TOL, (r, err)
+
+
 # one case per kernel path and operand form (m, n, k, group, dtype)
 ONE_HOT = [
     (1, 320, 1024, 128, "f16"),    # GEMV, four row groups share staged X
