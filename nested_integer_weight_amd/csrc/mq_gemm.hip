@@ -2,11 +2,13 @@
 //
 // Y[m, n] = sum_k X[m, k] * w_hat[n, k].  Per 64-wide k step a workgroup
 //  * copies its X tile (BM x 64, fp16/bf16) global -> VGPR -> LDS,
-//  * loads the packed planes of its weight tile (BN rows x two 32-code units),
-//    rebuilds and slices the codes in VGPRs and dequantizes them exactly in
-//    fp32 (w_hat = v*s + (delta - z)*s, all terms exact for an fp16 scale and
-//    an integer zero point), rounds once to the activation dtype and writes
-//    the tile to LDS,
+//  * loads the packed planes of its weight tile (BN rows x two 32-code units)
+//    and, at the first step of each quantization group, the group's scale and
+//    zero point, rebuilds and slices the codes in VGPRs and dequantizes them
+//    exactly in fp32 (w_hat = v*s + (delta - z)*s, exact for an fp16 scale
+//    and an integer zero point; computed from the exact fp16 halves 1024 + v
+//    with one fma per weight), rounds once to the activation dtype and
+//    writes the tile to LDS,
 //  * runs v_mfma_f32_16x16x32_{bf16,f16} from LDS with fp32 accumulators.
 // LDS is double buffered, so one barrier per step suffices: a step computes
 // from one buffer pair while the next step's tiles are written to the other.
