@@ -203,9 +203,16 @@ mq_status mq_linear_noalloc(const void* x, int32_t x_dtype, int32_t m, const mq_
  * Mix'n'Match blocks at their own widths); skinny-path calls (see mq_linear) with the same m,
  * width, rule, dtype and planned workgroup shape join one launch too (up to
  * 8 calls), each keeping its own k split as long as the workspace holds all
- * of them (mq_linear_mixed_workspace_bytes); the other calls run one by one.
- * The results are those of issuing the calls in order, bit for bit.  A launch
- * error reports the first call of its launch. */
+ * of them (mq_linear_mixed_workspace_bytes); calls on the MFMA GEMM's prefill
+ * tile (m > 128) with the same width, rule and dtype join launches without a k
+ * split (up to 32 calls each, the run's calls of that class cut into launches
+ * of equal size) when their output tiles of 256 x 256 number at least 224,
+ * which fills the GPU without splitting; the other calls run one by one.
+ * The results are those of issuing the calls in order, bit for bit, except
+ * that a call in a shared GEMM launch gives the result of mq_linear without a
+ * workspace (also bit for bit; with a workspace mq_linear may split k, which
+ * changes the summation order within the tolerance).  A launch error reports
+ * the first call of its launch. */
 mq_status mq_linear_mixed(const mq_call* calls, int32_t n_calls, void* workspace,
                           size_t workspace_bytes, int32_t* failed_call, void* stream);
 

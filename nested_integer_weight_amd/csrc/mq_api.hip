@@ -366,9 +366,39 @@ mq_status mq_linear_mixed(const mq_call* calls, int32_t n_calls, void* workspace
                  ? MQ_OK
                  : MQ_EHIP;
       } else {
-        done[t - i] = true;
-        st = run_linear(c.x, c.x_dtype, c.m, c.w, c.r, c.rule, c.group, c.scales, c.zeros, c.y, workspace,
-                        workspace_bytes, planes_of(c), static_cast<hipStream_t>(stream));
+        // prefill-tile calls of one width, rule and dtype share a launch
+        // without a k split when their tiles together fill the GPU; any
+        // other call runs alone (split over k where the workspace allows)
+        const LinearArgs a0 = call_args(c, planes_of(c));
+        LinearArgs la[kGemmMaxCalls];
+        int32_t idx[kGemmMaxCalls];
+        int nl = 0, tiles = 0;
+        if (gemm_batchable(a0)) {
+          // the class's calls in this run, cut into launches of equal size
+          int cnt = 0;
+          for (int32_t u = t; u < j; ++u)
+            if (!done[u - i] && !gemv_call(calls[u]) && !skinny_call(calls[u]) &&
+                same_gemm_launch(a0, call_args(calls[u], planes_of(calls[u]))))
+              ++cnt;
+          const int nlaunch = (cnt + kGemmMaxCalls - 1) / kGemmMaxCalls;
+          const int per = (cnt + nlaunch - 1) / (nlaunch > 0 ? nlaunch : 1);
+          for (int32_t u = t; u < j && nl < per; ++u) {
+            if (done[u - i] || gemv_call(calls[u]) || skinny_call(calls[u])) continue;
+            const LinearArgs au = call_args(calls[u], planes_of(calls[u]));
+            if (!same_gemm_launch(a0, au)) continue;
+            idx[nl] = u;
+            la[nl++] = au;
+            tiles += gemm_tiles(au);
+          }
+        }
+        if (nl >= 2 && tiles >= kGemmBatchMinTiles) {
+          for (int q = 0; q < nl; ++q) done[idx[q] - i] = true;
+          st = launch_gemm_multi(la, nl, static_cast<hipStream_t>(stream)) == hipSuccess ? MQ_OK : MQ_EHIP;
+        } else {
+          done[t - i] = true;
+          st = run_linear(c.x, c.x_dtype, c.m, c.w, c.r, c.rule, c.group, c.scales, c.zeros, c.y, workspace,
+                          workspace_bytes, planes_of(c), static_cast<hipStream_t>(stream));
+        }
       }
       if (st != MQ_OK) {
         if (failed_call) *failed_call = t;

@@ -348,28 +348,28 @@ struct GemmTile {
 
 // PP = 1 (eight-wave tiles): waves 4..7 take the stage-first order, so each
 // SIMD holds one wave of either order (waves are placed on the SIMDs in turn).
+// `block` is the workgroup's tile index within its call, `split` its k range.
 template <int R, int RULE, int BF16, int BM, int BN, int WM, int WN, int PP>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs a) {
+__device__ __forceinline__ void gemm_body(const GemmArgs& a, int block, int split, uint4 (&As)[2][BM * 8],
+                                          uint4 (&Bs)[2][BN / 16 * 2 * 64]) {
   using Tile = GemmTile<R, RULE, BF16, BM, BN, WM, WN>;
   static_assert(!PP || WM * WN == 8, "two orders need two waves per SIMD");
-  // double-buffered LDS tiles: X swizzled row-major, weights fragment-major
-  __shared__ uint4 As[2][BM * 8];
-  __shared__ uint4 Bs[2][BN / 16 * 2 * 64];
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % WM, wn = wave / WM;
 
   // ---- tile selection: workgroups sharing a weight tile land on one XCD ----
+  // (consecutive workgroups go to the eight XCDs in turn; a call's first
+  // workgroup is on XCD 0)
   const int G = a.tiles_m * a.tiles_n;
-  int logical = blockIdx.x;
-  if ((G & 7) == 0) logical = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  int logical = block;
+  if ((G & 7) == 0) logical = (block & 7) * (G >> 3) + (block >> 3);
   const int tm = logical % a.tiles_m, tn = logical / a.tiles_m;
   const int m0 = tm * BM, n0 = tn * BN;
 
   const int KT = a.k / BK;
-  const int kt_begin = blockIdx.y * a.ksteps_per_split;
+  const int kt_begin = split * a.ksteps_per_split;
   const int kt_end = min(KT, kt_begin + a.ksteps_per_split);
 
   // every k range is non-empty (the launcher sizes grid.y so)
@@ -394,7 +394,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs a) {
         if (m < a.m && n < a.n) {
           const float val = t.acc[i][j][v];
           if (a.to_workspace) {
-            static_cast<float*>(a.y)[((size_t)blockIdx.y * a.m + m) * a.n + n] = val;
+            static_cast<float*>(a.y)[((size_t)split * a.m + m) * a.n + n] = val;
           } else {
             uint16_t* y = static_cast<uint16_t*>(a.y) + (size_t)m * a.n + n;
             *y = (uint16_t)((BF16 ? pack_bf16x2(val, 0.f) : pack_f16x2(val, 0.f)) & 0xFFFFu);
@@ -403,6 +403,38 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs a) {
       }
     }
   }
+}
+
+template <int R, int RULE, int BF16, int BM, int BN, int WM, int WN, int PP>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs a) {
+  // double-buffered LDS tiles: X swizzled row-major, weights fragment-major
+  __shared__ uint4 As[2][BM * 8];
+  __shared__ uint4 Bs[2][BN / 16 * 2 * 64];
+  gemm_body<R, RULE, BF16, BM, BN, WM, WN, PP>(a, (int)blockIdx.x, (int)blockIdx.y, As, Bs);
+}
+
+// Independent calls of one launch class (width, rule, dtype, tile
+// configuration) in one launch, each without a k split: call i owns the
+// workgroups blk0[i] .. blk0[i] + tiles_i - 1 (blk0[i] a multiple of 8, so
+// the XCD grouping of a single launch is kept; the workgroups in between
+// exit at once).  A workgroup's call is found by a scalar search.
+struct GemmLaunch {
+  GemmArgs c[kGemmMaxCalls];
+  int blk0[kGemmMaxCalls];
+  int ncalls;
+};
+
+template <int R, int RULE, int BF16, int BM, int BN, int WM, int WN, int PP>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_multi_kernel(GemmLaunch L) {
+  __shared__ uint4 As[2][BM * 8];
+  __shared__ uint4 Bs[2][BN / 16 * 2 * 64];
+  const int b = (int)blockIdx.x;
+  int ci = 0;
+  while (ci + 1 < L.ncalls && b >= L.blk0[ci + 1]) ++ci;
+  const GemmArgs& a = L.c[ci];
+  const int local = b - L.blk0[ci];
+  if (local >= a.tiles_m * a.tiles_n) return;  // alignment padding: no tile
+  gemm_body<R, RULE, BF16, BM, BN, WM, WN, PP>(a, local, 0, As, Bs);
 }
 
 // Fixed-order sum of the split-k partials, then one rounding to the output dtype.
@@ -573,6 +605,77 @@ hipError_t launch_gemm(const LinearArgs& la, const GemmPlan& plan, void* workspa
   if (e != hipSuccess || splits == 1) return e;
   return launch_splitk_reduce(static_cast<const float*>(workspace), splits, (size_t)la.m * (size_t)la.n, la.y,
                               la.bf16, s);
+}
+
+bool gemm_batchable(const LinearArgs& a) { return a.m > 0 && pick_cfg(a.m, a.n) == 0; }
+bool same_gemm_launch(const LinearArgs& a, const LinearArgs& b) {
+  return gemm_batchable(a) && gemm_batchable(b) && a.r == b.r && a.rule == b.rule && a.bf16 == b.bf16;
+}
+int gemm_tiles(const LinearArgs& a) { return tiles_of(pick_cfg(a.m, a.n), a.m, a.n); }
+
+template <int R, int RULE, int BF16>
+static hipError_t gemm_multi_launch_t(const GemmLaunch& L, int blocks, hipStream_t s) {
+  hipLaunchKernelGGL((gemm_multi_kernel<R, RULE, BF16, 256, 256, 4, 2, 1>), dim3((unsigned)blocks), dim3(512), 0, s,
+                     L);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_multi(const LinearArgs* la, int ncalls, hipStream_t s) {
+  if (ncalls < 1 || ncalls > kGemmMaxCalls) return hipErrorInvalidValue;
+  // calls with the longest k first, so the workgroups with the most steps
+  // start first and the launch's tail is short
+  int ord[kGemmMaxCalls];
+  for (int i = 0; i < ncalls; ++i) {
+    if (!same_gemm_launch(la[0], la[i])) return hipErrorInvalidValue;
+    int p = i;
+    while (p > 0 && la[ord[p - 1]].k < la[i].k) {
+      ord[p] = ord[p - 1];
+      --p;
+    }
+    ord[p] = i;
+  }
+  GemmLaunch L;
+  int blocks = 0;
+  for (int q = 0; q < ncalls; ++q) {
+    const int i = ord[q];
+    GemmArgs& ga = L.c[q];
+    ga.x = la[i].x;
+    ga.y = la[i].y;
+    ga.pl = la[i].pl;
+    ga.scales = la[i].scales;
+    ga.zeros = la[i].zeros;
+    ga.m = la[i].m;
+    ga.n = la[i].n;
+    ga.k = la[i].k;
+    ga.group = la[i].group;
+    ga.tiles_m = cdiv(la[i].m, kCfgs[0].bm);
+    ga.tiles_n = cdiv(la[i].n, kCfgs[0].bn);
+    ga.ksteps_per_split = la[i].k / BK;
+    ga.to_workspace = 0;
+    L.blk0[q] = (blocks + 7) & ~7;
+    blocks = L.blk0[q] + ga.tiles_m * ga.tiles_n;
+  }
+  L.ncalls = ncalls;
+  const LinearArgs& a = la[0];
+#define MQ_GEMM_MULTI_CASE(RR)                                                                        \
+  case RR:                                                                                            \
+    if (a.rule == kRuleExtra)                                                                         \
+      return a.bf16 ? gemm_multi_launch_t<RR, kRuleExtra, 1>(L, blocks, s)                            \
+                    : gemm_multi_launch_t<RR, kRuleExtra, 0>(L, blocks, s);                           \
+    if (a.rule == kRuleRound)                                                                         \
+      return a.bf16 ? gemm_multi_launch_t<RR, kRuleRound, 1>(L, blocks, s)                            \
+                    : gemm_multi_launch_t<RR, kRuleRound, 0>(L, blocks, s);                           \
+    return a.bf16 ? gemm_multi_launch_t<RR, kRulePrefix, 1>(L, blocks, s)                             \
+                  : gemm_multi_launch_t<RR, kRulePrefix, 0>(L, blocks, s);
+  switch (a.r) {
+    MQ_GEMM_MULTI_CASE(2)
+    MQ_GEMM_MULTI_CASE(3)
+    MQ_GEMM_MULTI_CASE(4)
+    MQ_GEMM_MULTI_CASE(6)
+    MQ_GEMM_MULTI_CASE(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef MQ_GEMM_MULTI_CASE
 }
 
 hipError_t launch_splitk_reduce(const float* ws, int splits, size_t mn, void* y, int bf16, hipStream_t s) {

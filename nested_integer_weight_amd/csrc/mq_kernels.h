@@ -82,6 +82,17 @@ struct GemmPlan {
   int splits;    // split-k factor (1 = no workspace)
 };
 GemmPlan plan_gemm(int m, int n, int k, size_t workspace_bytes);
+// Up to kGemmMaxCalls independent calls of the prefill tile (m > 128) with the
+// same width, rule and dtype in one launch, none split over k.  Every output
+// sums its k steps in the same order whatever the tile configuration, split
+// or launch, so a call's result equals that of mq_linear without a workspace.
+// Worth it when the calls' tiles together fill the GPU (kGemmBatchMinTiles).
+constexpr int kGemmMaxCalls = 32;
+constexpr int kGemmBatchMinTiles = 224;
+bool gemm_batchable(const LinearArgs& a);
+bool same_gemm_launch(const LinearArgs& a, const LinearArgs& b);
+int gemm_tiles(const LinearArgs& a);
+hipError_t launch_gemm_multi(const LinearArgs* a, int ncalls, hipStream_t s);
 size_t gemm_workspace_bytes(int m, int n, int k);
 hipError_t launch_gemm(const LinearArgs& a, const GemmPlan& plan, void* workspace, hipStream_t s);
 

@@ -291,6 +291,28 @@ def test_mixed_equals_single_calls(mq):
         check_y(y, lay, lay.x, c.r, c.rule)
 
 
+# independent prefill-tile calls of one width, rule and dtype whose tiles fill
+# the GPU share one unsplit launch: each equals the single call made without a
+# workspace bit for bit (and so the oracle); ragged m and n, several k and groups
+@pytest.mark.parametrize("r,rule,dt", [(2, O.PREFIX, "bf16"), (8, O.PREFIX, "f16"), (4, O.ROUND, "bf16"),
+                                       (3, O.EXTRA, "bf16")])
+def test_mixed_gemm_calls_share_launch(mq, r, rule, dt):
+    shapes = [(257, 4096, 512, 64), (300, 4000, 768, 128), (257, 4096, 1024, 128), (260, 4352, 512, 256),
+              (257, 4096, 640, 128), (300, 3968, 512, 64), (257, 4096, 512, 128), (280, 4608, 768, 64)]
+    calls, lays = [], []
+    for i, (m, n, k, group) in enumerate(shapes):
+        lay = synth.make_layer(cfg_id=5, tensor_id=300 + i, n=n, k=k, m=m, group=group, x_dtype=dt)
+        q, s, z = to_dev(lay)
+        calls.append(mq.Call(x=lay.x.to(DEV), packed=mq.pack_parent(q).truncated(r, rule), r=r, rule=rule,
+                             group=group, scales=s, zeros=z))
+        lays.append(lay)
+    outs = mq.linear_mixed(calls)
+    for c, lay, y in zip(calls, lays, outs):
+        single = mq.linear(c.x, c.packed, c.r, c.rule, c.group, c.scales, c.zeros, workspace=None)
+        assert torch.equal(single, y)
+        check_y(y, lay, lay.x, c.r, c.rule)
+
+
 @pytest.mark.parametrize("m,dt,r,rule,group", [(1, "f16", 2, O.PREFIX, 128), (3, "f16", 3, O.ROUND, 64),
                                                 (1, "bf16", 8, O.PREFIX, 128), (2, "f16", 6, O.PREFIX, 256)])
 def test_mixed_batches_independent_gemv_calls(mq, m, dt, r, rule, group):
