@@ -313,6 +313,30 @@ def test_mixed_gemm_calls_share_launch(mq, r, rule, dt):
         check_y(y, lay, lay.x, c.r, c.rule)
 
 
+def test_mixed_gemm_batch_keeps_dependent_call_order(mq):
+    # eight independent prefill-tile calls share an unsplit launch; a ninth
+    # reads the first one's output (its own n equals k of the ninth) and must
+    # see it complete, so it runs after the shared launch
+    r, rule, group = 4, O.PREFIX, 128
+    calls, lays = [], []
+    for i in range(8):
+        lay = synth.make_layer(cfg_id=5, tensor_id=400 + i, n=4096, k=512, m=300, group=group, x_dtype="bf16")
+        q, s, z = to_dev(lay)
+        calls.append(mq.Call(x=lay.x.to(DEV), packed=mq.pack_parent(q), r=r, rule=rule, group=group,
+                             scales=s, zeros=z, out=torch.empty((300, 4096), dtype=torch.bfloat16, device=DEV)))
+        lays.append(lay)
+    dep = synth.make_layer(cfg_id=5, tensor_id=420, n=384, k=4096, m=0, group=group)
+    q, s, z = to_dev(dep)
+    pk_dep = mq.pack_parent(q)
+    calls.append(mq.Call(x=calls[0].out, packed=pk_dep, r=r, rule=rule, group=group, scales=s, zeros=z))
+    outs = mq.linear_mixed(calls)
+    for c, y in zip(calls[:8], outs[:8]):
+        assert torch.equal(y, mq.linear(c.x, c.packed, r, rule, group, c.scales, c.zeros, workspace=None))
+    want = mq.linear(outs[0], pk_dep, r, rule, group, s, z)
+    assert torch.equal(outs[8], want)
+    check_y(outs[8], dep, outs[0].cpu(), r, rule)
+
+
 @pytest.mark.parametrize("m,dt,r,rule,group", [(1, "f16", 2, O.PREFIX, 128), (3, "f16", 3, O.ROUND, 64),
                                                 (1, "bf16", 8, O.PREFIX, 128), (2, "f16", 6, O.PREFIX, 256)])
 def test_mixed_batches_independent_gemv_calls(mq, m, dt, r, rule, group):
